@@ -1,0 +1,144 @@
+/*
+ * sp24.h -- C ABI of libsp24: 2:4 structured-sparse compression and
+ * sparse x dense multiply-accumulate on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources: "CDNA and CDNA2 sparse MFMA builtins", sections
+ * "Structured sparsity (4:2 pattern)" and the builtin reference; "RDNA4
+ * sparse WMMA builtins", section "Structured sparsity (2:4 pattern)"; the ISA
+ * page for v_smfmac_f32_32x32x32_bf8_bf8, section "Semantics"):
+ *
+ *   A (M x K) keeps 2 of every 4 consecutive elements along K.  It is stored
+ *   as A_vals (M x K/2, the kept values in ascending position order) plus a
+ *   2-bit position code per kept value (the sparsity index).  The product is
+ *   D = alpha * expand(A_vals, meta) * B + beta * C, accumulated in fp32
+ *   (int32 for int8).
+ *
+ * Layouts (all row-major, dense leading dimensions, no padding):
+ *   A       M x K elements of the input type, K contiguous.
+ *   A_vals  M x K/2 elements of the same type.
+ *   meta    M x K/32 uint32 words.  The code (0..3, position inside its group
+ *           of 4) of compressed element c of row i is held in bits
+ *           [2*(c%16), 2*(c%16)+1] of meta[i*(K/32) + c/16].  With the
+ *           positions-0-and-2 pattern every byte reads 0x88, the index value
+ *           the pages' CDNA examples pass to the instruction.
+ *   B       K x N elements, N contiguous.  K is the dense K.
+ *   C / D   M x N float32 (int32 when both inputs are int8), updated in place.
+ *
+ * Element types (sp24_dtype): fp16 (IEEE binary16), bf16, int8 (two's
+ * complement), fp8 E4M3 and bf8 E5M2 (both OCP: E4M3 has no infinities and
+ * a largest finite value of 448).  Supported (a_type, b_type) pairs for
+ * sp24_gemm: (F16,F16), (BF16,BF16), (I8,I8), and any pair of the two 8-bit
+ * float types.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise; the caller owns
+ *     every buffer.  The library keeps no state between calls and allocates
+ *     no memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Calls only enqueue work on it; they never synchronise.  A kernel fault
+ *     shows up at the caller's next synchronisation.
+ *   - Argument errors are detected on the host, before anything is
+ *     launched, and returned as an sp24_status code; nothing is enqueued.
+ *   - Calls are thread-safe.
+ */
+#ifndef SP24_H
+#define SP24_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SP24_F16 = 1,
+  SP24_BF16 = 2,
+  SP24_I8 = 3,
+  SP24_FP8_E4M3 = 4,
+  SP24_BF8_E5M2 = 5
+} sp24_dtype;
+
+typedef enum {
+  SP24_OK = 0,
+  SP24_ERR_INVALID_VALUE = 1, /* bad shape, null pointer, overlap, workspace too small */
+  SP24_ERR_UNSUPPORTED = 2,   /* type pair, alpha/beta or leading dimension not supported */
+  SP24_ERR_MISALIGNED = 3,    /* a base pointer is not 16-byte aligned */
+  SP24_ERR_LAUNCH = 4         /* the HIP runtime refused the kernel launch */
+} sp24_status;
+
+/* Bytes of A_vals for an M x K matrix of `dtype`: M * (K/2) * element size.
+ * Returns 0 for an unknown dtype or negative sizes. */
+size_t sp24_values_bytes(int64_t M, int64_t K, int dtype);
+
+/* Bytes of the metadata for an M x K matrix: M * (K/32) * 4. */
+size_t sp24_meta_bytes(int64_t M, int64_t K);
+
+/* Workspace that sp24_gemm needs for this problem (currently always 0: the
+ * kernels reduce split-K partial sums on chip). */
+size_t sp24_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int a_type, int b_type);
+
+/*
+ * sp24_prune_compress -- dense A -> (A_vals, meta).
+ *
+ * Prunes every group of 4 consecutive K-elements of each row to its two
+ * largest-magnitude elements and compresses the result (pages: "walk the K
+ * dimension in groups of four, extract the two non-zero positions, and pack
+ * them consecutively"; which two to keep is not fixed by the pages, which
+ * leave pruning to an offline pass).  Magnitude is compared on the bit
+ * pattern with the sign cleared (float types; NaN ranks above Inf, -0 equals
+ * +0) or |x| (int8, -128 ranks highest); on equal magnitude the lower
+ * position wins.  Kept values are copied bit for bit.  An A that is already
+ * 2:4 is therefore compressed losslessly.
+ *
+ *   A       in:  M x K elements of `dtype`.
+ *   A_vals  out: M x K/2 elements (sp24_values_bytes).
+ *   meta    out: M x K/32 words (sp24_meta_bytes).
+ *   M, K    M >= 0, K >= 0, K % 32 == 0.  M == 0 or K == 0 enqueues nothing.
+ * Errors: INVALID_VALUE (shape, null pointer with nonzero size, A overlapping
+ * an output), UNSUPPORTED (unknown dtype), MISALIGNED (pointer not 16-byte
+ * aligned), LAUNCH.
+ */
+int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, int64_t K, int dtype,
+                        void* stream);
+
+/*
+ * sp24_gemm -- D = alpha * expand(A_vals, meta) * B + beta * C, D written
+ * over C.
+ *
+ * The hardware form is the sparse matrix-core instruction (pages: the index
+ * "aligns the compressed A elements against the correct rows of B"; the ISA
+ * page: "D = A (sparse) * B + D").  Products of the supported inputs are
+ * exact in fp32; sums are fp32 (exact int32 for int8).
+ *
+ *   A_vals, meta  compressed A as produced by sp24_prune_compress (or any
+ *                 caller-built data in the same layout; codes are trusted --
+ *                 a group whose two codes are not strictly increasing gives
+ *                 unspecified results).
+ *   a_type        element type of A_vals; b_type element type of B.
+ *   B             K x N elements of b_type.
+ *   C             in/out: M x N float32 (int32 for int8 x int8).  Not read
+ *                 when beta == 0 (NaN there does not propagate).
+ *   M, N, K       >= 0, K % 32 == 0, N * sizeof(b_type) % 16 == 0.
+ *                 M == 0 or N == 0: nothing is enqueued.  K == 0: D = beta*C.
+ *   alpha, beta   float scalars.  For int8: alpha must be 1, beta 0 or 1.
+ *   workspace     may be NULL when sp24_gemm_workspace_bytes() == 0.
+ * Errors: INVALID_VALUE (shape, null pointer, C overlapping an input,
+ * workspace too small), UNSUPPORTED (type pair, int8 alpha/beta, N*size not a
+ * multiple of 16 bytes), MISALIGNED, LAUNCH.
+ */
+int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, const void* B, int b_type, void* C,
+              int64_t M, int64_t N, int64_t K, float alpha, float beta, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* sp24_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int sp24_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SP24_H */

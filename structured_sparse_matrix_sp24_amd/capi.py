@@ -1,0 +1,153 @@
+"""ctypes binding of libsp24 (argument marshalling only).
+
+The functions named ``sp24_*`` mirror include/sp24.h one to one and take raw
+device pointers (ints) plus a HIP stream handle.  ``prune_compress`` and
+``gemm`` are torch conveniences: they allocate outputs with torch and pass
+``torch.cuda.current_stream()``.  Every step of the computation runs in the
+library's HIP kernels; if the library is missing this module raises -- there
+is no other path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsp24.so")
+
+SP24_F16, SP24_BF16, SP24_I8, SP24_FP8_E4M3, SP24_BF8_E5M2 = 1, 2, 3, 4, 5
+SP24_OK = 0
+_ESIZE = {SP24_F16: 2, SP24_BF16: 2, SP24_I8: 1, SP24_FP8_E4M3: 1, SP24_BF8_E5M2: 1}
+
+
+class Sp24Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {sp24_status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libsp24.so not built ({LIB_PATH}); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.sp24_values_bytes.argtypes = [I64, I64, I]
+        L.sp24_values_bytes.restype = SZ
+        L.sp24_meta_bytes.argtypes = [I64, I64]
+        L.sp24_meta_bytes.restype = SZ
+        L.sp24_gemm_workspace_bytes.argtypes = [I64, I64, I64, I, I]
+        L.sp24_gemm_workspace_bytes.restype = SZ
+        L.sp24_prune_compress.argtypes = [P, P, P, I64, I64, I, P]
+        L.sp24_prune_compress.restype = I
+        L.sp24_gemm.argtypes = [P, P, I, P, I, P, I64, I64, I64, F, F, P, SZ, P]
+        L.sp24_gemm.restype = I
+        L.sp24_status_string.argtypes = [I]
+        L.sp24_status_string.restype = ctypes.c_char_p
+        L.sp24_version.argtypes = []
+        L.sp24_version.restype = I
+        _lib = L
+    return _lib
+
+
+# ---- one-to-one C ABI mirrors ------------------------------------------------
+def sp24_values_bytes(M: int, K: int, dtype: int) -> int:
+    return lib().sp24_values_bytes(M, K, dtype)
+
+
+def sp24_meta_bytes(M: int, K: int) -> int:
+    return lib().sp24_meta_bytes(M, K)
+
+
+def sp24_gemm_workspace_bytes(M: int, N: int, K: int, a_type: int, b_type: int) -> int:
+    return lib().sp24_gemm_workspace_bytes(M, N, K, a_type, b_type)
+
+
+def sp24_prune_compress(A: int, A_vals: int, meta: int, M: int, K: int, dtype: int, stream: int | None) -> int:
+    return lib().sp24_prune_compress(A, A_vals, meta, M, K, dtype, stream)
+
+
+def sp24_gemm(A_vals: int, meta: int, a_type: int, B: int, b_type: int, C: int, M: int, N: int, K: int,
+              alpha: float, beta: float, workspace: int | None, workspace_bytes: int, stream: int | None) -> int:
+    return lib().sp24_gemm(A_vals, meta, a_type, B, b_type, C, M, N, K, alpha, beta, workspace, workspace_bytes,
+                           stream)
+
+
+def sp24_status_string(status: int) -> str:
+    return lib().sp24_status_string(status).decode()
+
+
+def sp24_version() -> int:
+    return lib().sp24_version()
+
+
+# ---- torch conveniences -------------------------------------------------------
+def torch_dtype(code: int):
+    import torch
+    return {SP24_F16: torch.float16, SP24_BF16: torch.bfloat16, SP24_I8: torch.int8,
+            SP24_FP8_E4M3: torch.float8_e4m3fn, SP24_BF8_E5M2: torch.float8_e5m2}[code]
+
+
+def dtype_code(t) -> int:
+    import torch
+    m = {torch.float16: SP24_F16, torch.bfloat16: SP24_BF16, torch.int8: SP24_I8,
+         torch.float8_e4m3fn: SP24_FP8_E4M3, torch.float8_e5m2: SP24_BF8_E5M2}
+    if t not in m:
+        raise TypeError(f"unsupported element type {t}")
+    return m[t]
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def prune_compress(A, dtype: int | None = None, stream=None):
+    """A: M x K device tensor (any 1- or 2-byte dtype holding the bits of
+    ``dtype``).  Returns (A_vals M x K/2 uint8/int16 view-compatible tensor
+    of the same element size, meta M x K/32 int32 tensor holding uint32 words)."""
+    import torch
+    if dtype is None:
+        dtype = dtype_code(A.dtype)
+    if A.dim() != 2 or not A.is_contiguous():
+        raise ValueError("A must be a contiguous 2-D tensor")
+    M, K = A.shape
+    vals = torch.empty((M, K // 2), dtype=A.dtype, device=A.device)
+    meta = torch.empty((M, K // 32), dtype=torch.int32, device=A.device)
+    st = sp24_prune_compress(A.data_ptr(), vals.data_ptr(), meta.data_ptr(), M, K, dtype, _stream(stream))
+    if st != SP24_OK:
+        raise Sp24Error(st, "sp24_prune_compress")
+    return vals, meta
+
+
+def gemm(A_vals, meta, B, C=None, alpha: float = 1.0, beta: float = 0.0, a_type: int | None = None,
+         b_type: int | None = None, stream=None):
+    """D = alpha * expand(A_vals, meta) @ B + beta * C, written into C (allocated
+    as zeros-free empty when C is None and beta == 0).  Returns C."""
+    import torch
+    if a_type is None:
+        a_type = dtype_code(A_vals.dtype)
+    if b_type is None:
+        b_type = dtype_code(B.dtype)
+    M, KC = A_vals.shape
+    K, N = B.shape
+    if K != 2 * KC:
+        raise ValueError(f"K mismatch: A_vals has {KC} compressed columns, B has {K} rows")
+    out_dtype = torch.int32 if (a_type == SP24_I8 and b_type == SP24_I8) else torch.float32
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C")
+        C = torch.empty((M, N), dtype=out_dtype, device=B.device)
+    for t in (A_vals, meta, B, C):
+        if not t.is_contiguous():
+            raise ValueError("all operands must be contiguous")
+    st = sp24_gemm(A_vals.data_ptr(), meta.data_ptr(), a_type, B.data_ptr(), b_type, C.data_ptr(), M, N, K,
+                   float(alpha), float(beta), None, 0, _stream(stream))
+    if st != SP24_OK:
+        raise Sp24Error(st, "sp24_gemm")
+    return C

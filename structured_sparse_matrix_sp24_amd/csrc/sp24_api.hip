@@ -1,0 +1,122 @@
+// Host side of the C ABI declared in include/sp24.h: argument checks,
+// kernel selection and launch on the caller's stream.
+#include <stdint.h>
+
+#include "sp24_internal.hpp"
+
+namespace sp24 {
+hipError_t launch_prune_compress(const void* A, void* vals, uint32_t* meta, int64_t M, int64_t K, int dtype,
+                                 hipStream_t stream);
+hipError_t launch_gemm(int op, const void* A_vals, const uint32_t* meta, const void* B, void* C, int M, int N, int K,
+                       float alpha, float beta, hipStream_t stream);
+}  // namespace sp24
+
+namespace {
+
+int esize(int dtype) {
+  switch (dtype) {
+    case SP24_F16: case SP24_BF16: return 2;
+    case SP24_I8: case SP24_FP8_E4M3: case SP24_BF8_E5M2: return 1;
+    default: return 0;
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) share a byte.
+bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  if (na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Sparse-MFMA operation for an (A, B) type pair, or -1.
+int op_for(int a, int b) {
+  using namespace sp24;
+  if (a == SP24_F16 && b == SP24_F16) return OP_F16;
+  if (a == SP24_BF16 && b == SP24_BF16) return OP_BF16;
+  if (a == SP24_I8 && b == SP24_I8) return OP_I8;
+  if (a == SP24_FP8_E4M3 && b == SP24_FP8_E4M3) return OP_FP8_FP8;
+  if (a == SP24_FP8_E4M3 && b == SP24_BF8_E5M2) return OP_FP8_BF8;
+  if (a == SP24_BF8_E5M2 && b == SP24_FP8_E4M3) return OP_BF8_FP8;
+  if (a == SP24_BF8_E5M2 && b == SP24_BF8_E5M2) return OP_BF8_BF8;
+  return -1;
+}
+
+constexpr int64_t kMaxDim = 0x7FFFFFFF;
+
+}  // namespace
+
+extern "C" {
+
+size_t sp24_values_bytes(int64_t M, int64_t K, int dtype) {
+  const int es = esize(dtype);
+  if (es == 0 || M < 0 || K < 0) return 0;
+  return (size_t)M * (size_t)(K / 2) * (size_t)es;
+}
+
+size_t sp24_meta_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0) return 0;
+  return (size_t)M * (size_t)(K / 32) * 4u;
+}
+
+size_t sp24_gemm_workspace_bytes(int64_t, int64_t, int64_t, int, int) { return 0; }
+
+int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, int64_t K, int dtype,
+                        void* stream) {
+  const int es = esize(dtype);
+  if (es == 0) return SP24_ERR_UNSUPPORTED;
+  if (M < 0 || K < 0 || K % 32 != 0 || M > kMaxDim || K > kMaxDim) return SP24_ERR_INVALID_VALUE;
+  if (M == 0 || K == 0) return SP24_OK;
+  if (!A || !A_vals || !meta) return SP24_ERR_INVALID_VALUE;
+  if (!aligned16(A) || !aligned16(A_vals) || !aligned16(meta)) return SP24_ERR_MISALIGNED;
+  const uint64_t a_bytes = (uint64_t)M * K * es;
+  const uint64_t v_bytes = sp24_values_bytes(M, K, dtype), m_bytes = sp24_meta_bytes(M, K);
+  if (overlap(A, a_bytes, A_vals, v_bytes) || overlap(A, a_bytes, meta, m_bytes) ||
+      overlap(A_vals, v_bytes, meta, m_bytes))
+    return SP24_ERR_INVALID_VALUE;
+  const hipError_t e =
+      sp24::launch_prune_compress(A, A_vals, meta, M, K, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SP24_OK : SP24_ERR_LAUNCH;
+}
+
+int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, const void* B, int b_type, void* C, int64_t M,
+              int64_t N, int64_t K, float alpha, float beta, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  const int op = op_for(a_type, b_type);
+  if (op < 0) return SP24_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return SP24_ERR_INVALID_VALUE;
+  const int ea = esize(a_type), eb = esize(b_type);
+  if (((uint64_t)N * eb) % 16 != 0) return SP24_ERR_UNSUPPORTED;
+  if (op == sp24::OP_I8 && (alpha != 1.0f || (beta != 0.0f && beta != 1.0f))) return SP24_ERR_UNSUPPORTED;
+  if (workspace_bytes < sp24_gemm_workspace_bytes(M, N, K, a_type, b_type)) return SP24_ERR_INVALID_VALUE;
+  (void)workspace;
+  if (M == 0 || N == 0) return SP24_OK;
+  if (!C) return SP24_ERR_INVALID_VALUE;
+  if (K > 0 && (!A_vals || !meta || !B)) return SP24_ERR_INVALID_VALUE;
+  if (!aligned16(C) || (K > 0 && (!aligned16(A_vals) || !aligned16(meta) || !aligned16(B))))
+    return SP24_ERR_MISALIGNED;
+  const uint64_t c_bytes = (uint64_t)M * N * 4;
+  if (K > 0 && (overlap(C, c_bytes, A_vals, (uint64_t)M * (K / 2) * ea) ||
+                overlap(C, c_bytes, meta, (uint64_t)M * (K / 32) * 4) || overlap(C, c_bytes, B, (uint64_t)K * N * eb)))
+    return SP24_ERR_INVALID_VALUE;
+  const hipError_t e = sp24::launch_gemm(op, A_vals, meta, B, C, (int)M, (int)N, (int)K, alpha, beta,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SP24_OK : SP24_ERR_LAUNCH;
+}
+
+const char* sp24_status_string(int status) {
+  switch (status) {
+    case SP24_OK: return "SP24_OK";
+    case SP24_ERR_INVALID_VALUE: return "SP24_ERR_INVALID_VALUE";
+    case SP24_ERR_UNSUPPORTED: return "SP24_ERR_UNSUPPORTED";
+    case SP24_ERR_MISALIGNED: return "SP24_ERR_MISALIGNED";
+    case SP24_ERR_LAUNCH: return "SP24_ERR_LAUNCH";
+    default: return "SP24_ERR_UNKNOWN";
+  }
+}
+
+int sp24_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,424 @@
+// sp24_gemm: D = alpha * expand(A_vals, meta) * B + beta * C on the gfx950
+// sparse matrix cores (v_smfmac_*_16x16x64 for 16-bit inputs, *_16x16x128 for
+// 8-bit inputs).
+//
+// What the instruction computes ("CDNA and CDNA2 sparse MFMA builtins",
+// builtin reference and section "Structured sparsity"; ISA page for
+// v_smfmac_f32_32x32x32_bf8_bf8, section "Semantics"): one 16x16 tile
+// D += expand(A, idx) * B with A held compressed.  The register layouts used
+// here were pinned on gfx950 with probe kernels (the pages print only the
+// older CDNA shapes):
+//   A   lane l holds row l%16; its 16 bytes are 4 (16-bit) or 8 (8-bit)
+//       groups of K; lane group ga = l/16.
+//   B   lane l holds column l%16; 32 bytes; lane group gb = l/16.
+//   idx each lane's own register: code of its compressed element e at bits
+//       2e (+16 if ABID is odd, for 16-bit inputs).
+//   D   lane l, register r = element (4*(l/16) + r, l%16)  (the pages'
+//       16x16 accumulator layout).
+//   Group q of A lane group ga meets B lane group gb = 2*(ga%2) + q/H at its
+//   group slot t = H*(ga/2) + q%H, where H = groups per A lane / 2.
+//
+// K mapping chosen from that pairing (per k-step of KS dense columns): A lane
+// group ga reads its 16 contiguous compressed bytes [16*ga, 16*ga + 16), so a
+// B lane group gb needs two runs of K:
+//   16-bit:  k in [8gb, 8gb+8)  and [32+8gb, 32+8gb+8)      (KS = 64)
+//   8-bit:   k in [16gb, 16gb+16) and [64+16gb, 64+16gb+16) (KS = 128)
+// which the LDS transpose reads (ds_read_b64_tr_b16 / _b8) deliver 4 or 8 k
+// at a time from a row-major (k, n) tile.
+#include "sp24_internal.hpp"
+
+namespace sp24 {
+
+// ----------------------------------------------------------------------------
+// Large-tile kernel: 256 x 256 output tile per workgroup, 4 waves in 2 x 2,
+// each wave 128 x 128 = 8 x 8 instruction tiles (256 accumulator registers).
+// Per k-step the workgroup stages A_vals (256 rows x 64 B), meta (256 rows x
+// 8 or 16 B) and B (KS rows x 512 or 256 B) into LDS with buffer loads that
+// write LDS directly; three stages are in flight.
+// ----------------------------------------------------------------------------
+constexpr int kBM = 256, kBN = 256, kThreads = 256;
+constexpr int kLdsA = kBM * 64;    // 16 KiB
+constexpr int kLdsB = 32768;       // KS * BN * esize = 32 KiB for both families
+constexpr int kLdsM = kBM * 16;    // 4 KiB (16-bit inputs use half)
+
+// A tile: row r, 16-byte chunk c stored at chunk c ^ swzA(r) (conflict-free
+// for 16 lanes reading 16 consecutive rows at one chunk).
+__device__ __forceinline__ int swzA(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
+// B tile, 16-bit: row k holds 256 columns = 16 pairs of chunks; pair p stored
+// at p ^ swzB16(k).  8-bit: 16 chunks per row; chunk c stored at c ^ swzB8(k).
+__device__ __forceinline__ int swzB16(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
+__device__ __forceinline__ int swzB8(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
+
+template <int OP>
+struct Stage {
+  SP24_LDS char* a;
+  SP24_LDS char* b;
+  SP24_LDS char* m;
+};
+
+template <int OP>
+__device__ __forceinline__ void issue_stage(const Stage<OP>& st, const char* A_vals, const char* meta, const char* B,
+                                            int m0, int n0, int M, int N, int K, int ks) {
+  constexpr int KS = op_kstep(OP), ES = op_esize(OP);
+  const int w = threadIdx.x >> 6, l = opaque(lane_id());
+  const int64_t rowA = (int64_t)K / 2 * ES;   // bytes per compressed row
+  const int64_t rowM = (int64_t)K / 8;        // bytes per metadata row
+  // ---- A: 16 instructions of 16 rows x 64 B, 4 per wave
+  {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(A_vals + (int64_t)m0 * rowA, (int64_t)(M - m0) * rowA);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = w * 4 + i;
+      const int row = j * 16 + (l >> 2);
+      const int c = (l & 3) ^ swzA(row);
+      const int64_t col = (int64_t)ks * 64 + 16 * c;  // byte column in the compressed row
+      const uint32_t off = col < rowA ? (uint32_t)(row * rowA + col) : kOOB;
+      dma16(r, st.a + j * 1024, off);
+    }
+  }
+  // ---- B: 32 instructions of 1 KiB, 8 per wave
+  {
+    const int64_t kb = (int64_t)ks * KS;
+    const int64_t start = (kb * N + n0) * ES;
+    const int64_t total = (int64_t)K * N * ES;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(B + start, total - start);
+    const int64_t ldb = (int64_t)N * ES;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = w * 8 + i;
+      int row, c;
+      if constexpr (ES == 2) {
+        row = j * 2 + (l >> 5);
+        const int p = l & 31;
+        c = (((p >> 1) ^ swzB16(row)) << 1) | (p & 1);
+      } else {
+        row = j * 4 + (l >> 4);
+        c = (l & 15) ^ swzB8(row);
+      }
+      dma16(r, st.b + j * 1024, (uint32_t)(row * ldb + 16 * c));
+    }
+  }
+  // ---- meta
+  {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(meta + (int64_t)m0 * rowM, (int64_t)(M - m0) * rowM);
+    if constexpr (ES == 2) {
+      // 256 rows x 8 B: 8 instructions of 4 B per lane, 2 per wave
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int j = w * 2 + i;
+        const int row = j * 32 + (l >> 1);
+        dma4(r, st.m + j * 256, (uint32_t)(row * rowM + ks * 8 + 4 * (l & 1)));
+      }
+    } else {
+      // 256 rows x 16 B: 4 instructions of 16 B per lane, 1 per wave
+      const int row = w * 64 + l;
+      dma16(r, st.m + w * 1024, (uint32_t)(row * rowM + ks * 16));
+    }
+  }
+}
+
+// Loads issued per wave per stage (vmcnt budget).
+template <int OP>
+constexpr int loads_per_stage() { return op_esize(OP) == 2 ? 4 + 8 + 2 : 4 + 8 + 1; }
+
+template <int OP>
+__device__ __forceinline__ void compute_stage(const Stage<OP>& st, i32x4 (&acc)[8][8]) {
+  constexpr int ES = op_esize(OP);
+  const int w = threadIdx.x >> 6, l = opaque(lane_id());
+  const int wm = w >> 1, wn = w & 1;
+  const int ga = l >> 4;
+  i32x4 a[8];
+  int idx[8];
+#pragma unroll
+  for (int tm = 0; tm < 8; ++tm) {
+    const int row = wm * 128 + tm * 16 + (l & 15);
+    a[tm] = *(SP24_LDS i32x4*)(st.a + row * 64 + 16 * (ga ^ swzA(row)));
+    if constexpr (ES == 2) idx[tm] = *(SP24_LDS unsigned short*)(st.m + row * 8 + 2 * ga);
+    else idx[tm] = *(SP24_LDS int*)(st.m + row * 16 + 4 * ga);
+  }
+  const int gb = l >> 4, s = l & 15;
+#pragma unroll
+  for (int tn = 0; tn < 8; ++tn) {
+    const int ct = wn * 8 + tn;  // 16-column tile index inside the 256-wide B tile
+    i32x2 p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (ES == 2) {
+        const int k = 8 * gb + 4 * (r & 1) + 32 * (r >> 1) + (s >> 2);
+        const int addr = k * 512 + ((ct ^ swzB16(k)) << 5) + (s & 3) * 8;
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SP24_LDS i16x4*)(st.b + addr));
+        p[r] = __builtin_bit_cast(i32x2, v);
+      } else {
+        const int k = 16 * gb + 8 * (r & 1) + 64 * (r >> 1) + (s >> 1);
+        const int addr = k * 256 + ((ct ^ swzB8(k)) << 4) + (s & 1) * 8;
+        p[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SP24_LDS i32x2*)(st.b + addr));
+      }
+    }
+    const i32x8 b = {p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm) acc[tm][tn] = smfmac16<OP>(acc[tm][tn], a[tm], b, idx[tm]);
+  }
+}
+
+template <int OP>
+__global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(const char* __restrict__ A_vals,
+                                                                  const char* __restrict__ meta,
+                                                                  const char* __restrict__ B, void* C, int M, int N,
+                                                                  int K, float alpha, float beta, int tiles_m,
+                                                                  int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char lA0[kLdsA], lA1[kLdsA], lA2[kLdsA];
+  __shared__ __attribute__((aligned(1024))) char lB0[kLdsB], lB1[kLdsB], lB2[kLdsB];
+  __shared__ __attribute__((aligned(1024))) char lM0[kLdsM], lM1[kLdsM], lM2[kLdsM];
+  const Stage<OP> s0{(SP24_LDS char*)lA0, (SP24_LDS char*)lB0, (SP24_LDS char*)lM0};
+  const Stage<OP> s1{(SP24_LDS char*)lA1, (SP24_LDS char*)lB1, (SP24_LDS char*)lM1};
+  const Stage<OP> s2{(SP24_LDS char*)lA2, (SP24_LDS char*)lB2, (SP24_LDS char*)lM2};
+
+  // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
+  // contiguous range of tiles so neighbouring tiles share its L2, then walk
+  // that range in groups of 8 tile-rows.
+  const int ntiles = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((ntiles & 7) == 0) t = (t & 7) * (ntiles >> 3) + (t >> 3);
+  constexpr int GM = 8;
+  const int group = t / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int in_group = t - group * GM * tiles_n;
+  const int tm_ = first_m + in_group % gsize;
+  const int tn_ = in_group / gsize;
+  const int m0 = tm_ * kBM, n0 = tn_ * kBN;
+
+  constexpr int KS = op_kstep(OP);
+  const int nsteps = (K + KS - 1) / KS;
+  i32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+  constexpr int LPS = loads_per_stage<OP>();
+  if (nsteps > 0) issue_stage<OP>(s0, A_vals, meta, B, m0, n0, M, N, K, 0);
+  if (nsteps > 1) issue_stage<OP>(s1, A_vals, meta, B, m0, n0, M, N, K, 1);
+  auto step = [&](const Stage<OP>& cur, const Stage<OP>& next2, int ks) {
+    if (ks + 1 < nsteps) waitcnt<LPS, 0>();
+    else waitcnt<0, 0>();
+    __builtin_amdgcn_s_barrier();
+    if (ks + 2 < nsteps) issue_stage<OP>(next2, A_vals, meta, B, m0, n0, M, N, K, ks + 2);
+    compute_stage<OP>(cur, acc);
+  };
+  // Main loop over whole rounds of the three buffers, then at most two more
+  // steps.  (A single loop with early exits gives the register allocator
+  // several live states at once and it spills.)
+  int ks = 0;
+  for (; ks + 3 <= nsteps; ks += 3) {
+    step(s0, s2, ks);
+    step(s1, s0, ks + 1);
+    step(s2, s1, ks + 2);
+  }
+  if (ks < nsteps) step(s0, s2, ks);
+  if (ks + 1 < nsteps) step(s1, s0, ks + 1);
+
+  // ---- epilogue: D = alpha * acc + beta * C  (int8: acc + C when beta == 1)
+  const int w = threadIdx.x >> 6, l = lane_id();
+  const int wm = w >> 1, wn = w & 1;
+#pragma unroll
+  for (int tm = 0; tm < 8; ++tm) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + wm * 128 + tm * 16 + 4 * (l >> 4) + r;
+      if (row >= M) continue;
+#pragma unroll
+      for (int tn = 0; tn < 8; ++tn) {
+        const int col = n0 + wn * 128 + tn * 16 + (l & 15);
+        if (col >= N) continue;
+        const int64_t o = (int64_t)row * N + col;
+        if constexpr (op_is_int(OP)) {
+          int* D = static_cast<int*>(C);
+          const int v = acc[tm][tn][r];
+          D[o] = beta != 0.0f ? v + D[o] : v;
+        } else {
+          // cast the whole vector: a bit cast of one vector element is not safe here
+          const f32x4 fv = __builtin_bit_cast(f32x4, acc[tm][tn]);
+          float* D = static_cast<float*>(C);
+          const float v = fv[r] * alpha;
+          D[o] = beta != 0.0f ? v + beta * D[o] : v;
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Small-N kernel (N <= 64): A is read from HBM exactly once.  A workgroup of
+// 8 waves owns one 16-row tile and all N columns; the waves split the
+// k-steps round-robin, each staging its own B slice (KS x N) through LDS for
+// the transpose reads, and the 8 partial tiles are summed on chip in a fixed
+// order (deterministic).
+// ----------------------------------------------------------------------------
+constexpr int kSmallWaves = 8;
+constexpr int kSmallBSlice = 64 * 64 * 2;  // KS * N * esize bytes, N <= 64
+
+template <int OP>
+__global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const char* __restrict__ A_vals,
+                                                                        const char* __restrict__ meta,
+                                                                        const char* __restrict__ B, void* C, int M,
+                                                                        int N, int K, float alpha, float beta) {
+  constexpr int KS = op_kstep(OP), ES = op_esize(OP);
+  __shared__ __attribute__((aligned(1024))) char lB[kSmallWaves][2][kSmallBSlice];
+  const int w = threadIdx.x >> 6, l = lane_id();
+  const int m0 = blockIdx.x * 16;
+  const int ga = l >> 4, gb = l >> 4, s = l & 15;
+  const int nt = (N + 15) >> 4;
+  const int nsteps = (K + KS - 1) / KS;
+  const int64_t rowA = (int64_t)K / 2 * ES, rowM = (int64_t)K / 8;
+  const int ldb = N * ES;                 // bytes per B row (multiple of 16)
+  const int chunks_per_row = ldb >> 4;
+  const int slice_instr = (KS * ldb) >> 10;  // 1 KiB per DMA instruction (KS*ldb is a multiple of 1 KiB)
+  const int row = m0 + (l & 15);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A_vals + (int64_t)m0 * rowA, (int64_t)(M - m0) * rowA);
+  const __amdgpu_buffer_rsrc_t rm = make_rsrc(meta + (int64_t)m0 * rowM, (int64_t)(M - m0) * rowM);
+  const int64_t btotal = (int64_t)K * ldb;
+
+  i32x4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  // Register prefetch of A and idx, LDS double buffer of the B slice.
+  auto fetch = [&](int ks, int buf, i32x4& a, int& idx) {
+    const int64_t col = (int64_t)ks * 64 + 16 * ga;
+    const uint32_t offa = col < rowA ? (uint32_t)((l & 15) * rowA + col) : kOOB;
+    a = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)offa, 0, 0);
+    if constexpr (ES == 2) idx = (int)__builtin_amdgcn_raw_buffer_load_b16(rm, (int)((l & 15) * rowM + ks * 8 + 2 * ga), 0, 0);
+    else idx = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, (int)((l & 15) * rowM + ks * 16 + 4 * ga), 0, 0);
+    const int64_t start = (int64_t)ks * KS * ldb;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + start, btotal - start);
+    for (int j = 0; j < slice_instr; ++j) {
+      const int q = j * 64 + l;  // chunk index inside the slice
+      const int brow = q / chunks_per_row, bc = q - brow * chunks_per_row;
+      dma16(rb, (SP24_LDS char*)lB[w][buf] + j * 1024, (uint32_t)(brow * ldb + 16 * bc));
+    }
+  };
+  i32x4 a_cur, a_nxt;
+  int i_cur = 0, i_nxt = 0;
+  int ks = w, buf = 0;
+  if (ks < nsteps) fetch(ks, 0, a_cur, i_cur);
+  for (; ks < nsteps; ks += kSmallWaves) {
+    const int ksn = ks + kSmallWaves;
+    if (ksn < nsteps) fetch(ksn, buf ^ 1, a_nxt, i_nxt);
+    // wait for everything except the prefetch just issued
+    if (ksn < nsteps) {
+      switch (slice_instr) {  // the prefetch is 2 + slice_instr loads
+        case 1: waitcnt<3>(); break;
+        case 2: waitcnt<4>(); break;
+        case 3: waitcnt<5>(); break;
+        case 4: waitcnt<6>(); break;
+        case 5: waitcnt<7>(); break;
+        case 6: waitcnt<8>(); break;
+        case 7: waitcnt<9>(); break;
+        default: waitcnt<10>(); break;
+      }
+    } else {
+      waitcnt<0>();
+    }
+    const SP24_LDS char* sb = (const SP24_LDS char*)lB[w][buf];
+    for (int tn = 0; tn < nt; ++tn) {
+      i32x2 p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (ES == 2) {
+          const int k = 8 * gb + 4 * (r & 1) + 32 * (r >> 1) + (s >> 2);
+          const int addr = k * ldb + tn * 32 + (s & 3) * 8;
+          p[r] = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((SP24_LDS i16x4*)(sb + addr)));
+        } else {
+          const int k = 16 * gb + 8 * (r & 1) + 64 * (r >> 1) + (s >> 1);
+          const int addr = k * ldb + tn * 16 + (s & 1) * 8;
+          p[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SP24_LDS i32x2*)(sb + addr));
+        }
+      }
+      const i32x8 b = {p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+      acc[tn] = smfmac16<OP>(acc[tn], a_cur, b, i_cur);
+    }
+    a_cur = a_nxt;
+    i_cur = i_nxt;
+    buf ^= 1;
+  }
+  // ---- reduce the 8 partial tiles in LDS (fixed order), then epilogue
+  waitcnt<0, 0>();
+  __syncthreads();
+  int* red = (int*)&lB[0][0][0];  // 8 waves x 4 tiles x 64 lanes x 4 regs x 4 B = 32 KiB
+  for (int tn = 0; tn < nt; ++tn)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[((w * 4 + tn) * 4 + r) * 64 + l] = acc[tn][r];
+  __syncthreads();
+  // thread t handles output element (i, j) = (t / 64 .. ) of the 16 x N tile
+  for (int e = threadIdx.x; e < 16 * nt * 16; e += kSmallWaves * 64) {
+    const int tn = e >> 8, within = e & 255;
+    const int i = within >> 4, j = within & 15;
+    const int lane = 16 * (i >> 2) + j, r = i & 3;
+    const int grow = m0 + i, gcol = tn * 16 + j;
+    if (grow >= M || gcol >= N) continue;
+    const int64_t o = (int64_t)grow * N + gcol;
+    if constexpr (op_is_int(OP)) {
+      int sum = 0;
+      for (int ww = 0; ww < kSmallWaves; ++ww) sum += red[((ww * 4 + tn) * 4 + r) * 64 + lane];
+      int* D = static_cast<int*>(C);
+      D[o] = beta != 0.0f ? sum + D[o] : sum;
+    } else {
+      float sum = 0.0f;
+      for (int ww = 0; ww < kSmallWaves; ++ww) sum += __int_as_float(red[((ww * 4 + tn) * 4 + r) * 64 + lane]);
+      float* D = static_cast<float*>(C);
+      const float v = alpha * sum;
+      D[o] = beta != 0.0f ? v + beta * D[o] : v;
+    }
+  }
+}
+
+// ---- K == 0: D = beta * C ---------------------------------------------------
+template <bool INT>
+__global__ void scale_c_kernel(void* C, int64_t n, float beta) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  if constexpr (INT) {
+    int* D = static_cast<int*>(C);
+    D[i] = beta != 0.0f ? D[i] : 0;
+  } else {
+    float* D = static_cast<float*>(C);
+    D[i] = beta != 0.0f ? beta * D[i] : 0.0f;
+  }
+}
+
+template <int OP>
+static hipError_t launch_op(const void* A_vals, const uint32_t* meta, const void* B, void* C, int M, int N, int K,
+                            float alpha, float beta, hipStream_t stream) {
+  const char* a = static_cast<const char*>(A_vals);
+  const char* m = reinterpret_cast<const char*>(meta);
+  const char* b = static_cast<const char*>(B);
+  if (K == 0) {
+    const int64_t n = (int64_t)M * N;
+    hipLaunchKernelGGL((scale_c_kernel<op_is_int(OP)>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, C, n,
+                       beta);
+    return hipGetLastError();
+  }
+  if (N <= 64) {
+    hipLaunchKernelGGL((gemm_smalln_kernel<OP>), dim3((unsigned)((M + 15) / 16)), dim3(kSmallWaves * 64), 0, stream,
+                       a, m, b, C, M, N, K, alpha, beta);
+    return hipGetLastError();
+  }
+  const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+  hipLaunchKernelGGL((gemm_large_kernel<OP>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0, stream, a, m, b,
+                     C, M, N, K, alpha, beta, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(int op, const void* A_vals, const uint32_t* meta, const void* B, void* C, int M, int N, int K,
+                       float alpha, float beta, hipStream_t stream) {
+  switch (op) {
+    case OP_F16: return launch_op<OP_F16>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+    case OP_BF16: return launch_op<OP_BF16>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+    case OP_I8: return launch_op<OP_I8>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+    case OP_FP8_FP8: return launch_op<OP_FP8_FP8>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+    case OP_FP8_BF8: return launch_op<OP_FP8_BF8>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+    case OP_BF8_FP8: return launch_op<OP_BF8_FP8>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+    case OP_BF8_BF8: return launch_op<OP_BF8_BF8>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sp24

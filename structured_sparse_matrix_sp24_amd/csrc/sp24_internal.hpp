@@ -1,0 +1,100 @@
+// Internal helpers shared by the libsp24 kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sp24.h"
+
+namespace sp24 {
+
+#define SP24_LDS __attribute__((address_space(3)))
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Sparse-MFMA operation, one per supported (A type, B type) pair.
+enum Op { OP_F16 = 0, OP_BF16, OP_I8, OP_FP8_FP8, OP_FP8_BF8, OP_BF8_FP8, OP_BF8_BF8, OP_COUNT };
+
+__host__ __device__ constexpr bool op_is_8bit(int op) { return op >= OP_I8; }
+__host__ __device__ constexpr bool op_is_int(int op) { return op == OP_I8; }
+// Dense K consumed by one 16x16 sparse instruction: 64 for 16-bit inputs, 128 for 8-bit.
+__host__ __device__ constexpr int op_kstep(int op) { return op_is_8bit(op) ? 128 : 64; }
+__host__ __device__ constexpr int op_esize(int op) { return op_is_8bit(op) ? 1 : 2; }
+
+// One 16x16 sparse MFMA step.  Per lane: `a` = 16 bytes of compressed A
+// (8 values for 16-bit types, 16 for 8-bit), `b` = 32 bytes of dense B,
+// `idx` = this lane's 2-bit position codes (bits 2e.. for its element e; for
+// 16-bit types ABID picks the 16-bit half of idx).  Accumulator is 4 x fp32
+// (or int32 for int8) in the 16x16 layout lane = 16*(i/4) + j, reg = i%4.
+template <int OP, int ABID = 0>
+__device__ __forceinline__ i32x4 smfmac16(i32x4 acc, i32x4 a, i32x8 b, int idx) {
+  if constexpr (OP == OP_F16) {
+    f32x4 c = __builtin_bit_cast(f32x4, acc);
+    c = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x16, b), c,
+                                                   idx, 0, ABID);
+    return __builtin_bit_cast(i32x4, c);
+  } else if constexpr (OP == OP_BF16) {
+    f32x4 c = __builtin_bit_cast(f32x4, acc);
+    c = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x16, b), c,
+                                                    idx, 0, ABID);
+    return __builtin_bit_cast(i32x4, c);
+  } else if constexpr (OP == OP_I8) {
+    return __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, acc, idx, 0, 0);
+  } else {
+    f32x4 c = __builtin_bit_cast(f32x4, acc);
+    if constexpr (OP == OP_FP8_FP8) c = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, b, c, idx, 0, 0);
+    else if constexpr (OP == OP_FP8_BF8) c = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_bf8(a, b, c, idx, 0, 0);
+    else if constexpr (OP == OP_BF8_FP8) c = __builtin_amdgcn_smfmac_f32_16x16x128_bf8_fp8(a, b, c, idx, 0, 0);
+    else c = __builtin_amdgcn_smfmac_f32_16x16x128_bf8_bf8(a, b, c, idx, 0, 0);
+    return __builtin_bit_cast(i32x4, c);
+  }
+}
+
+// ---- buffer resources: raw byte-addressed, hardware range-checked ----------
+// Reads at offsets >= num_records return zeros, which is how ragged edges and
+// the K tail are handled without branches.
+#define SP24_RSRC_WORD3 0x00020000
+static constexpr uint32_t kOOB = 0x7FFFFFF0u;          // offset used for masked lanes
+static constexpr uint64_t kMaxRecords = 0x7FFFFF00ull;  // keep every range below kOOB
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  uint32_t n = (uint32_t)(bytes < kMaxRecords ? bytes : kMaxRecords);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, SP24_RSRC_WORD3);
+}
+
+// 16 bytes per lane from global memory straight into LDS.  The LDS address is
+// lds_base + 16 * lane (wave-uniform base).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, SP24_LDS void* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, (int)voff, 0, 0, 0);
+}
+// 4 bytes per lane; LDS address lds_base + 4 * lane.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, SP24_LDS void* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 4, (int)voff, 0, 0, 0);
+}
+
+// s_waitcnt with only vmcnt (and lgkmcnt) constrained (gfx9 encoding).
+template <int VM, int LGKM = 15>
+__device__ __forceinline__ void waitcnt() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+// A copy of v the compiler cannot see through.  Addresses derived from it are
+// recomputed where they are used (a few VALU ops that co-issue with MFMA)
+// instead of being hoisted out of the K loop and held in registers.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+}  // namespace sp24
