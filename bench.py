@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the 2:4 sparse hot path on one MI355X.
+
+One step = sp24_prune_compress(A) followed by sp24_gemm(A_vals, meta, B) on a
+seeded synthetic workload (default: fp16, M = N = K = 8192, A and B ~ N(0,1),
+A pruned to 2:4 by the compress kernel, fp32 output, beta = 0).  Inputs are
+resident in HBM before the timed region; the timed region is exactly --steps
+steps bracketed by torch.cuda.synchronize().
+
+Prints ONE JSON line: value = dense-equivalent TFLOP/s of the whole step
+(2*M*N*K per step / step time); `roofline` describes the dominant kernel
+(the GEMM) against the sparse-MFMA peak, timed with HIP events on the stream
+the kernels run on; `cpu_baseline` times the CPU oracle on a bounded row
+sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks.  The sparse matrix-core peak is twice the dense one
+# (one 16x16x64 fp16 smfmac = 32768 dense-equivalent flop per 16 cycles per
+# SIMD: 1024 SIMDs * 2048 flop/clk * 2.4 GHz = 5033 TFLOP/s).
+PEAK_SPARSE_TFLOPS = {"fp16": 5033.2, "bf16": 5033.2, "int8": 10066.3, "fp8": 10066.3}
+PEAK_HBM_GBPS = 8000.0
+
+WORKLOADS = {
+    # name -> (workload key, dtype label)
+    "f16_8192": "fp16",
+    "f16_4096": "fp16",
+    "bf16_linear_n16": "bf16",
+    "bf16_linear_n4096": "bf16",
+    "i8_8192": "int8",
+    "fp8_bf8_8192x16384": "fp8",
+    "bf8_bf8_8192x16384": "fp8",
+}
+
+
+def src_hash(*rel):
+    h = hashlib.sha256()
+    for r in rel:
+        with open(os.path.join(ROOT, r), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, kernel_src_hash):
+    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE),
+    scaled by the same counters' reading for a plain copy of known size.
+    Returned only if taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_src_hash") != kernel_src_hash:
+        return None
+    return t.get("gemm_bytes_per_launch")
+
+
+def cpu_baseline(w, rows, max_threads=16):
+    """Time the oracle (as it stands) on `rows` rows of the workload on the
+    host cores: prune+compress of those rows of A and those rows of the
+    product (full N and K)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(cores, max_threads, rows))
+    A = np.ascontiguousarray(w.A[:rows])
+    bounds = np.linspace(0, rows, threads + 1).astype(int)
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda i: oracle.prune_compress(A[bounds[i]:bounds[i + 1]], w.a_type), range(threads)))
+    t1 = time.perf_counter()
+    if w.a_type == oracle.I8:
+        work = lambda i: oracle.gemm_i64(parts[i][0], parts[i][1], w.B)  # noqa: E731
+    else:
+        work = lambda i: oracle.gemm_f64(parts[i][0], parts[i][1], w.a_type, w.B, w.b_type, want_abs=False)  # noqa: E731
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(work, range(threads)))
+    t2 = time.perf_counter()
+    flops = 2.0 * rows * w.N * w.K
+    return {
+        "value": round(flops / (t2 - t0) / 1e12, 6),
+        "unit": "TFLOP/s (dense-equivalent, prune+compress+product)",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{rows} of {w.M} rows: prune+compress of those rows of A and those rows of the product "
+                  f"(full N={w.N}, K={w.K}); fp64/int64 plain C, one row block per thread",
+        "compress_s": round(t1 - t0, 3),
+        "product_s": round(t2 - t1, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="f16_8192", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the oracle sample (default: sized to ~15 s)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--gemm-only-launches", type=int, default=0,
+                    help="after the timed steps, launch only the GEMM this many times (for profilers)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the 2:4 path has no inter-GPU step); "
+              "--gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import structured_sparse_matrix_sp24_amd as pkg
+    from structured_sparse_matrix_sp24_amd import workloads as wl
+
+    pkg.sp24_version()  # fails loudly if libsp24.so is missing
+    dev = torch.device("cuda:0")
+    w = wl.make(args.workload)
+    label = WORKLOADS[args.workload]
+    tview = {wl.F16: (np.int16, torch.float16), wl.BF16: (np.int16, torch.bfloat16), wl.I8: (np.int8, torch.int8),
+             wl.E4M3: (np.uint8, torch.float8_e4m3fn), wl.E5M2: (np.uint8, torch.float8_e5m2)}
+
+    def up(bits, t):
+        nv, tv = tview[t]
+        return torch.from_numpy(np.ascontiguousarray(bits).view(nv)).to(dev).view(tv)
+
+    A = up(w.A, w.a_type)
+    B = up(w.B, w.b_type)
+    out_dtype = torch.int32 if w.a_type == wl.I8 else torch.float32
+    C = torch.from_numpy(w.C).to(dev) if w.C is not None else torch.empty((w.M, w.N), dtype=out_dtype, device=dev)
+    C0 = C.clone() if w.beta != 0.0 else None
+    vals = torch.empty((w.M, w.K // 2), dtype=A.dtype, device=dev)
+    meta = torch.empty((w.M, w.K // 32), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def compress():
+        st = pkg.sp24_prune_compress(A.data_ptr(), vals.data_ptr(), meta.data_ptr(), w.M, w.K, w.a_type, sh)
+        if st:
+            raise pkg.Sp24Error(st, "sp24_prune_compress")
+
+    def gemm():
+        st = pkg.sp24_gemm(vals.data_ptr(), meta.data_ptr(), w.a_type, B.data_ptr(), w.b_type, C.data_ptr(),
+                           w.M, w.N, w.K, w.alpha, w.beta, None, 0, sh)
+        if st:
+            raise pkg.Sp24Error(st, "sp24_gemm")
+
+    def reset_c():
+        if C0 is not None:  # beta != 0: keep each step's C input identical
+            C.copy_(C0)
+
+    for _ in range(args.warmup):
+        reset_c()
+        compress()
+        gemm()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        e0, e1, e2 = ev[s]
+        e0.record(stream)
+        compress()
+        e1.record(stream)
+        gemm()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if C0 is not None:
+        # the timed loop accumulated beta*C repeatedly; restore and run one clean step
+        reset_c()
+        compress()
+        gemm()
+        torch.cuda.synchronize()
+    comp_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    gemm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    for _ in range(args.gemm_only_launches):
+        gemm()
+    torch.cuda.synchronize()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    flop = 2.0 * w.M * w.N * w.K
+    es_a = wl.ESIZE[w.a_type]
+    es_b = wl.ESIZE[w.b_type]
+    comp_bytes = es_a * w.M * w.K + es_a * w.M * w.K // 2 + w.M * w.K // 8
+    gemm_bytes = es_a * w.M * w.K // 2 + w.M * w.K // 8 + es_b * w.K * w.N + 4 * w.M * w.N * (
+        2 if w.beta != 0.0 else 1)
+    gemm_tflops = flop / (gemm_ms * 1e-3) / 1e12
+    comp_gbps = comp_bytes / (comp_ms * 1e-3) / 1e9
+    gemm_gbps = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+    khash = src_hash("structured_sparse_matrix_sp24_amd/csrc/sp24_gemm.hip",
+                     "structured_sparse_matrix_sp24_amd/csrc/sp24_internal.hpp")
+    hbm_bound = w.N <= 64
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(gemm_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(gemm_gbps / PEAK_HBM_GBPS, 4), "traffic": load_traffic(args.workload, khash),
+                "kernel": "sp24 gemm (small-N)", "kernel_ms": round(gemm_ms, 5),
+                "algorithmic_bytes": gemm_bytes}
+    else:
+        peak = PEAK_SPARSE_TFLOPS[label]
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(gemm_tflops / peak, 4), "traffic": load_traffic(args.workload, khash),
+                "kernel": "sp24 gemm (256x256 tile)", "kernel_ms": round(gemm_ms, 5),
+                "algorithmic_flop": flop}
+    res = {
+        "metric": "dense-equiv TFLOP/s of 2:4 sparse GEMM (fp16, 8192^3) + % of smfmac peak",
+        "value": round(flop / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp16": "f16", "bf16": "bf16", "int8": "i8", "fp8": "fp8"}[label] + "->f32" if label != "int8"
+        else "i8->i32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": w.M, "N": w.N, "K": w.K, "a_type": wl_name(w.a_type),
+                   "b_type": wl_name(w.b_type), "alpha": w.alpha, "beta": w.beta,
+                   "step": "sp24_prune_compress(A) + sp24_gemm(A_vals, meta, B, C)"},
+        "gemm_tflops": round(gemm_tflops, 1),
+        "gemm_frac_sparse_peak": round(gemm_tflops / PEAK_SPARSE_TFLOPS[label], 4),
+        "gemm_ms": round(gemm_ms, 5),
+        "compress_ms": round(comp_ms, 5),
+        "compress_gbps": round(comp_gbps, 1),
+        "compress_frac_hbm": round(comp_gbps / PEAK_HBM_GBPS, 4),
+        "roofline": roof,
+        "kernel_src_hash": khash,
+    }
+    if not args.no_cpu:
+        rows = args.cpu_rows
+        if rows is None:
+            # the oracle does ~0.6e9 multiply-adds per second per core: ~1.6e11 of them is 10-30 s on 16 cores
+            rows = max(1, min(w.M, int(1.6e11 / max(1, w.N * w.K // 2))))
+        res["cpu_baseline"] = cpu_baseline(w, rows)
+    print(json.dumps(res), flush=True)
+
+
+def wl_name(t):
+    return {1: "fp16", 2: "bf16", 3: "int8", 4: "fp8_e4m3", 5: "bf8_e5m2"}[t]
+
+
+if __name__ == "__main__":
+    main()
