@@ -31,10 +31,16 @@ namespace sp24 {
 
 // ----------------------------------------------------------------------------
 // Large-tile kernel: 256 x 256 output tile per workgroup, 4 waves in 2 x 2,
-// each wave 128 x 128 = 8 x 8 instruction tiles (256 accumulator registers).
-// Per k-step the workgroup stages A_vals (256 rows x 64 B), meta (256 rows x
-// 8 or 16 B) and B (KS rows x 512 or 256 B) into LDS with buffer loads that
-// write LDS directly; three stages are in flight.
+// each wave 128 x 128 = 8 x 8 instruction tiles (256 accumulator registers,
+// one wave per SIMD).  Per k-step the workgroup stages A_vals (256 rows x
+// 64 B), meta (256 rows x 8 or 16 B) and B (KS rows x 512 or 256 B) into LDS
+// with buffer loads that write LDS directly; three stages are in flight.
+//
+// Each k-step is split into two halves of four column tiles.  The barrier
+// that publishes the next stage sits between the halves, and the next
+// stage's fragment reads are issued right after it, so the second half's
+// MFMAs cover the LDS latency.  All per-lane addresses are computed once;
+// inside the loop a stage costs a handful of scalar ops plus immediates.
 // ----------------------------------------------------------------------------
 constexpr int kBM = 256, kBN = 256, kThreads = 256;
 constexpr int kLdsA = kBM * 64;    // 16 KiB
@@ -46,74 +52,123 @@ constexpr int kLdsM = kBM * 16;    // 4 KiB (16-bit inputs use half)
 __device__ __forceinline__ int swzA(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
 // B tile, 16-bit: row k holds 256 columns = 16 pairs of chunks; pair p stored
 // at p ^ swzB16(k).  8-bit: 16 chunks per row; chunk c stored at c ^ swzB8(k).
+// For the rows one transpose read touches these depend only on the lane, so
+// a lane's read address is a per-lane constant plus immediates.
 __device__ __forceinline__ int swzB16(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
 __device__ __forceinline__ int swzB8(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
 
-template <int OP>
 struct Stage {
   SP24_LDS char* a;
   SP24_LDS char* b;
   SP24_LDS char* m;
 };
 
+// Per-lane constants, computed once per workgroup.
+struct LaneConsts {
+  uint32_t voA[4];  // DMA byte offsets of this lane's A chunks (k-step 0)
+  uint32_t voB[8];  // DMA byte offsets of this lane's B chunks within a k-step slice
+  uint32_t voM[2];  // DMA byte offsets of this lane's metadata (k-step 0)
+  int ldsA;         // LDS offset of this lane's A fragment for tm = 0
+  int ldsM;         // LDS offset of this lane's index half-word / word for tm = 0
+  int ldsB[8];      // LDS offset of this lane's transpose read for column tile tn (r = 0)
+};
+
+struct Frags {
+  i32x4 a[8];
+  int idx[8];
+};
+struct BHalf {
+  i32x8 b[4];
+};
+
 template <int OP>
-__device__ __forceinline__ void issue_stage(const Stage<OP>& st, const char* A_vals, const char* meta, const char* B,
-                                            int m0, int n0, int M, int N, int K, int ks) {
+__device__ __forceinline__ LaneConsts make_lane_consts(int w, int l, int64_t rowA, int64_t rowM, int ldb) {
+  constexpr int ES = op_esize(OP);
+  LaneConsts c;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (w * 4 + i) * 16 + (l >> 2);
+    c.voA[i] = (uint32_t)(row * rowA + 16 * ((l & 3) ^ swzA(row)));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = w * 8 + i;
+    int row, ch;
+    if constexpr (ES == 2) {
+      row = j * 2 + (l >> 5);
+      const int p = l & 31;
+      ch = (((p >> 1) ^ swzB16(row)) << 1) | (p & 1);
+    } else {
+      row = j * 4 + (l >> 4);
+      ch = (l & 15) ^ swzB8(row);
+    }
+    c.voB[i] = (uint32_t)(row * ldb + 16 * ch);
+  }
+  if constexpr (ES == 2) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) c.voM[i] = (uint32_t)(((w * 2 + i) * 32 + (l >> 1)) * rowM + 4 * (l & 1));
+  } else {
+    c.voM[0] = (uint32_t)((w * 64 + l) * rowM);
+    c.voM[1] = 0;
+  }
+  const int wm = w >> 1, wn = w & 1, ga = l >> 4, r16 = l & 15;
+  c.ldsA = (wm * 128 + r16) * 64 + 16 * (ga ^ swzA(r16));
+  c.ldsM = ES == 2 ? (wm * 128 + r16) * 8 + 2 * ga : (wm * 128 + r16) * 16 + 4 * ga;
+  const int gb = l >> 4, s = l & 15;
+#pragma unroll
+  for (int tn = 0; tn < 8; ++tn) {
+    const int ct = wn * 8 + tn;
+    if constexpr (ES == 2) {
+      const int k0 = 8 * gb + (s >> 2);
+      c.ldsB[tn] = k0 * 512 + ((ct ^ swzB16(k0)) << 5) + (s & 3) * 8;
+    } else {
+      const int k0 = 16 * gb + (s >> 1);
+      c.ldsB[tn] = k0 * 256 + ((ct ^ swzB8(k0)) << 4) + (s & 1) * 8;
+    }
+  }
+  return c;
+}
+
+// Issue the DMA of one k-step into a stage.  `full` = the k-step lies wholly
+// inside K (every step but possibly the last); the last step of a K that is
+// not a multiple of KS masks the A chunks past the row end.
+template <int OP>
+__device__ __forceinline__ void issue_stage(const Stage& st, const LaneConsts& lc, __amdgpu_buffer_rsrc_t rA,
+                                            __amdgpu_buffer_rsrc_t rM, const char* B, int64_t btotal, int n0, int N,
+                                            int64_t rowA, int w, int ks, bool full) {
   constexpr int KS = op_kstep(OP), ES = op_esize(OP);
-  const int w = threadIdx.x >> 6, l = opaque(lane_id());
-  const int64_t rowA = (int64_t)K / 2 * ES;   // bytes per compressed row
-  const int64_t rowM = (int64_t)K / 8;        // bytes per metadata row
-  // ---- A: 16 instructions of 16 rows x 64 B, 4 per wave
-  {
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(A_vals + (int64_t)m0 * rowA, (int64_t)(M - m0) * rowA);
+  const int l = lane_id();
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, st.a + (w * 4 + i) * 1024, 16, (int)lc.voA[i], ks * 64, 0, 0);
+  } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = w * 4 + i;
-      const int row = j * 16 + (l >> 2);
-      const int c = (l & 3) ^ swzA(row);
-      const int64_t col = (int64_t)ks * 64 + 16 * c;  // byte column in the compressed row
-      const uint32_t off = col < rowA ? (uint32_t)(row * rowA + col) : kOOB;
-      dma16(r, st.a + j * 1024, off);
+      const int row = (w * 4 + i) * 16 + (l >> 2);
+      const int64_t col = (int64_t)ks * 64 + 16 * ((l & 3) ^ swzA(row));
+      const uint32_t off = col < rowA ? lc.voA[i] + (uint32_t)(ks * 64) : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, st.a + (w * 4 + i) * 1024, 16, (int)off, 0, 0, 0);
     }
   }
-  // ---- B: 32 instructions of 1 KiB, 8 per wave
-  {
-    const int64_t kb = (int64_t)ks * KS;
-    const int64_t start = (kb * N + n0) * ES;
-    const int64_t total = (int64_t)K * N * ES;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(B + start, total - start);
-    const int64_t ldb = (int64_t)N * ES;
+  const int64_t start = ((int64_t)ks * KS * N + n0) * ES;
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(B + start, btotal - start);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = w * 8 + i;
-      int row, c;
-      if constexpr (ES == 2) {
-        row = j * 2 + (l >> 5);
-        const int p = l & 31;
-        c = (((p >> 1) ^ swzB16(row)) << 1) | (p & 1);
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, st.b + (w * 8 + i) * 1024, 16, (int)lc.voB[i], 0, 0, 0);
+  if constexpr (ES == 2) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (full) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rM, st.m + (w * 2 + i) * 256, 4, (int)lc.voM[i], ks * 8, 0, 0);
       } else {
-        row = j * 4 + (l >> 4);
-        c = (l & 15) ^ swzB8(row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rM, st.m + (w * 2 + i) * 256, 4, (int)(lc.voM[i] + ks * 8), 0, 0,
+                                                 0);
       }
-      dma16(r, st.b + j * 1024, (uint32_t)(row * ldb + 16 * c));
     }
-  }
-  // ---- meta
-  {
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(meta + (int64_t)m0 * rowM, (int64_t)(M - m0) * rowM);
-    if constexpr (ES == 2) {
-      // 256 rows x 8 B: 8 instructions of 4 B per lane, 2 per wave
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int j = w * 2 + i;
-        const int row = j * 32 + (l >> 1);
-        dma4(r, st.m + j * 256, (uint32_t)(row * rowM + ks * 8 + 4 * (l & 1)));
-      }
-    } else {
-      // 256 rows x 16 B: 4 instructions of 16 B per lane, 1 per wave
-      const int row = w * 64 + l;
-      dma16(r, st.m + w * 1024, (uint32_t)(row * rowM + ks * 16));
-    }
+  } else {
+    if (full) __builtin_amdgcn_raw_ptr_buffer_load_lds(rM, st.m + w * 1024, 16, (int)lc.voM[0], ks * 16, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(rM, st.m + w * 1024, 16, (int)(lc.voM[0] + ks * 16), 0, 0, 0);
   }
 }
 
@@ -122,42 +177,55 @@ template <int OP>
 constexpr int loads_per_stage() { return op_esize(OP) == 2 ? 4 + 8 + 2 : 4 + 8 + 1; }
 
 template <int OP>
-__device__ __forceinline__ void compute_stage(const Stage<OP>& st, i32x4 (&acc)[8][8]) {
+__device__ __forceinline__ void read_a(const Stage& st, const LaneConsts& lc, Frags& f) {
   constexpr int ES = op_esize(OP);
-  const int w = threadIdx.x >> 6, l = opaque(lane_id());
-  const int wm = w >> 1, wn = w & 1;
-  const int ga = l >> 4;
-  i32x4 a[8];
-  int idx[8];
 #pragma unroll
   for (int tm = 0; tm < 8; ++tm) {
-    const int row = wm * 128 + tm * 16 + (l & 15);
-    a[tm] = *(SP24_LDS i32x4*)(st.a + row * 64 + 16 * (ga ^ swzA(row)));
-    if constexpr (ES == 2) idx[tm] = *(SP24_LDS unsigned short*)(st.m + row * 8 + 2 * ga);
-    else idx[tm] = *(SP24_LDS int*)(st.m + row * 16 + 4 * ga);
+    f.a[tm] = *(const SP24_LDS i32x4*)(st.a + lc.ldsA + tm * 1024);
+    if constexpr (ES == 2) f.idx[tm] = *(const SP24_LDS unsigned short*)(st.m + lc.ldsM + tm * 128);
+    else f.idx[tm] = *(const SP24_LDS int*)(st.m + lc.ldsM + tm * 256);
   }
-  const int gb = l >> 4, s = l & 15;
+}
+
+// B fragments of column tiles 4H .. 4H+3: four transpose reads each, at row
+// offsets +0, +4 (or +8), +32 (or +64) and +36 (or +72) from the lane's base,
+// which are byte offsets 0, 2048, 16384, 18432 for both element sizes.
+template <int OP, int H>
+__device__ __forceinline__ void read_b(const Stage& st, const LaneConsts& lc, BHalf& h) {
+  constexpr int ES = op_esize(OP);
 #pragma unroll
-  for (int tn = 0; tn < 8; ++tn) {
-    const int ct = wn * 8 + tn;  // 16-column tile index inside the 256-wide B tile
-    i32x2 p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (ES == 2) {
-        const int k = 8 * gb + 4 * (r & 1) + 32 * (r >> 1) + (s >> 2);
-        const int addr = k * 512 + ((ct ^ swzB16(k)) << 5) + (s & 3) * 8;
-        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SP24_LDS i16x4*)(st.b + addr));
-        p[r] = __builtin_bit_cast(i32x2, v);
-      } else {
-        const int k = 16 * gb + 8 * (r & 1) + 64 * (r >> 1) + (s >> 1);
-        const int addr = k * 256 + ((ct ^ swzB8(k)) << 4) + (s & 1) * 8;
-        p[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SP24_LDS i32x2*)(st.b + addr));
-      }
+  for (int t = 0; t < 4; ++t) {
+    const SP24_LDS char* p = st.b + lc.ldsB[4 * H + t];
+    i32x2 q[4];
+    if constexpr (ES == 2) {
+      q[0] = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((SP24_LDS i16x4*)(p)));
+      q[1] = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((SP24_LDS i16x4*)(p + 2048)));
+      q[2] = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((SP24_LDS i16x4*)(p + 16384)));
+      q[3] = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((SP24_LDS i16x4*)(p + 18432)));
+    } else {
+      q[0] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SP24_LDS i32x2*)(p));
+      q[1] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SP24_LDS i32x2*)(p + 2048));
+      q[2] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SP24_LDS i32x2*)(p + 16384));
+      q[3] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SP24_LDS i32x2*)(p + 18432));
     }
-    const i32x8 b = {p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
-#pragma unroll
-    for (int tm = 0; tm < 8; ++tm) acc[tm][tn] = smfmac16<OP>(acc[tm][tn], a[tm], b, idx[tm]);
+    h.b[t] = i32x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
   }
+}
+
+template <int OP, int H>
+__device__ __forceinline__ void mma_half(i32x4 (&acc)[8][8], const Frags& f, const BHalf& h) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm) acc[tm][4 * H + t] = smfmac16<OP>(acc[tm][4 * H + t], f.a[tm], h.b[t], f.idx[tm]);
+}
+
+// Workgroup barrier that the compiler may not move memory operations across
+// (the data behind it was written by other waves' direct-to-LDS loads).
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <int OP>
@@ -169,9 +237,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(const char* __r
   __shared__ __attribute__((aligned(1024))) char lA0[kLdsA], lA1[kLdsA], lA2[kLdsA];
   __shared__ __attribute__((aligned(1024))) char lB0[kLdsB], lB1[kLdsB], lB2[kLdsB];
   __shared__ __attribute__((aligned(1024))) char lM0[kLdsM], lM1[kLdsM], lM2[kLdsM];
-  const Stage<OP> s0{(SP24_LDS char*)lA0, (SP24_LDS char*)lB0, (SP24_LDS char*)lM0};
-  const Stage<OP> s1{(SP24_LDS char*)lA1, (SP24_LDS char*)lB1, (SP24_LDS char*)lM1};
-  const Stage<OP> s2{(SP24_LDS char*)lA2, (SP24_LDS char*)lB2, (SP24_LDS char*)lM2};
+  const Stage s0{(SP24_LDS char*)lA0, (SP24_LDS char*)lB0, (SP24_LDS char*)lM0};
+  const Stage s1{(SP24_LDS char*)lA1, (SP24_LDS char*)lB1, (SP24_LDS char*)lM1};
+  const Stage s2{(SP24_LDS char*)lA2, (SP24_LDS char*)lB2, (SP24_LDS char*)lM2};
+  constexpr int KS = op_kstep(OP), ES = op_esize(OP);
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous range of tiles so neighbouring tiles share its L2, then walk
@@ -184,12 +253,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(const char* __r
   const int first_m = group * GM;
   const int gsize = min(tiles_m - first_m, GM);
   const int in_group = t - group * GM * tiles_n;
-  const int tm_ = first_m + in_group % gsize;
-  const int tn_ = in_group / gsize;
-  const int m0 = tm_ * kBM, n0 = tn_ * kBN;
+  const int m0 = (first_m + in_group % gsize) * kBM;
+  const int n0 = (in_group / gsize) * kBN;
 
-  constexpr int KS = op_kstep(OP);
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int l = lane_id();
+  const int64_t rowA = (int64_t)K / 2 * ES;  // bytes per compressed row
+  const int64_t rowM = (int64_t)K / 8;       // bytes per metadata row
+  const int ldb = N * ES;
+  const LaneConsts lc = make_lane_consts<OP>(w, l, rowA, rowM, ldb);
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A_vals + (int64_t)m0 * rowA, (int64_t)(M - m0) * rowA);
+  const __amdgpu_buffer_rsrc_t rM = make_rsrc(meta + (int64_t)m0 * rowM, (int64_t)(M - m0) * rowM);
+  const int64_t btotal = (int64_t)K * N * ES;
   const int nsteps = (K + KS - 1) / KS;
+  const int nfull = K / KS;  // steps that lie wholly inside K
+
   i32x4 acc[8][8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -197,29 +275,60 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(const char* __r
     for (int j = 0; j < 8; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
   constexpr int LPS = loads_per_stage<OP>();
-  if (nsteps > 0) issue_stage<OP>(s0, A_vals, meta, B, m0, n0, M, N, K, 0);
-  if (nsteps > 1) issue_stage<OP>(s1, A_vals, meta, B, m0, n0, M, N, K, 1);
-  auto step = [&](const Stage<OP>& cur, const Stage<OP>& next2, int ks) {
-    if (ks + 1 < nsteps) waitcnt<LPS, 0>();
-    else waitcnt<0, 0>();
-    __builtin_amdgcn_s_barrier();
-    if (ks + 2 < nsteps) issue_stage<OP>(next2, A_vals, meta, B, m0, n0, M, N, K, ks + 2);
-    compute_stage<OP>(cur, acc);
+  auto issue = [&](const Stage& st, int ks) {
+    issue_stage<OP>(st, lc, rA, rM, B, btotal, n0, N, rowA, w, ks, ks < nfull);
   };
-  // Main loop over whole rounds of the three buffers, then at most two more
-  // steps.  (A single loop with early exits gives the register allocator
-  // several live states at once and it spills.)
-  int ks = 0;
-  for (; ks + 3 <= nsteps; ks += 3) {
-    step(s0, s2, ks);
-    step(s1, s0, ks + 1);
-    step(s2, s1, ks + 2);
+  // Two register sets (X, Y) for the fragments of consecutive steps and
+  // three LDS stages: the roles repeat every 6 steps, so the loop is unrolled
+  // 6 times and no fragment is ever copied between registers.
+  Frags fX, fY;
+  BHalf b1X, b1Y, b2;
+  if (nsteps > 0) {
+    issue(s0, 0);
+    if (nsteps > 1) issue(s1, 1);
+    if (nsteps > 1) waitcnt<LPS, 0>();
+    else waitcnt<0, 0>();
+    stage_barrier();
+    if (nsteps > 2) issue(s2, 2);
+    read_a<OP>(s0, lc, fX);
+    read_b<OP, 0>(s0, lc, b1X);
   }
-  if (ks < nsteps) step(s0, s2, ks);
-  if (ks + 1 < nsteps) step(s1, s0, ks + 1);
+  // One k-step on stage `cur` with fragments (fc, b1c); step ks+1 lives in
+  // stage `nxt` and its fragments go to (fn, b1n).  The DMA of step ks+3
+  // reuses `cur` once every wave has passed the barrier (all reads of `cur`
+  // have completed by then).
+  auto step = [&](const Stage& cur, const Stage& nxt, int ks, Frags& fc, BHalf& b1c, Frags& fn, BHalf& b1n) {
+    read_b<OP, 1>(cur, lc, b2);
+    mma_half<OP, 0>(acc, fc, b1c);
+    if (ks + 1 < nsteps) {
+      if (ks + 2 < nsteps) waitcnt<LPS, 0>();
+      else waitcnt<0, 0>();
+      stage_barrier();
+      if (ks + 3 < nsteps) issue(cur, ks + 3);
+      read_a<OP>(nxt, lc, fn);
+      read_b<OP, 0>(nxt, lc, b1n);
+    }
+    mma_half<OP, 1>(acc, fc, b2);
+  };
+  // Whole rounds of six steps, then up to five more (a single loop with early
+  // exits gives the register allocator several live states at once and it
+  // spills).
+  int ks = 0;
+  for (; ks + 6 <= nsteps; ks += 6) {
+    step(s0, s1, ks + 0, fX, b1X, fY, b1Y);
+    step(s1, s2, ks + 1, fY, b1Y, fX, b1X);
+    step(s2, s0, ks + 2, fX, b1X, fY, b1Y);
+    step(s0, s1, ks + 3, fY, b1Y, fX, b1X);
+    step(s1, s2, ks + 4, fX, b1X, fY, b1Y);
+    step(s2, s0, ks + 5, fY, b1Y, fX, b1X);
+  }
+  if (ks + 0 < nsteps) step(s0, s1, ks + 0, fX, b1X, fY, b1Y);
+  if (ks + 1 < nsteps) step(s1, s2, ks + 1, fY, b1Y, fX, b1X);
+  if (ks + 2 < nsteps) step(s2, s0, ks + 2, fX, b1X, fY, b1Y);
+  if (ks + 3 < nsteps) step(s0, s1, ks + 3, fY, b1Y, fX, b1X);
+  if (ks + 4 < nsteps) step(s1, s2, ks + 4, fX, b1X, fY, b1Y);
 
   // ---- epilogue: D = alpha * acc + beta * C  (int8: acc + C when beta == 1)
-  const int w = threadIdx.x >> 6, l = lane_id();
   const int wm = w >> 1, wn = w & 1;
 #pragma unroll
   for (int tm = 0; tm < 8; ++tm) {
