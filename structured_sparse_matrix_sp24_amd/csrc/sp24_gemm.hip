@@ -62,6 +62,8 @@ struct Stage {
   SP24_LDS char* b;
   SP24_LDS char* m;
 };
+constexpr int kLdsStage = kLdsA + kLdsB + kLdsM;  // 52 KiB; three stages = 156 KiB
+__device__ __forceinline__ Stage stage_of(SP24_LDS char* base) { return Stage{base, base + kLdsA, base + kLdsA + kLdsB}; }
 
 // Per-lane constants, computed once per workgroup.
 struct LaneConsts {
@@ -133,42 +135,40 @@ __device__ __forceinline__ LaneConsts make_lane_consts(int w, int l, int64_t row
 // inside K (every step but possibly the last); the last step of a K that is
 // not a multiple of KS masks the A chunks past the row end.
 template <int OP>
-__device__ __forceinline__ void issue_stage(const Stage& st, const LaneConsts& lc, __amdgpu_buffer_rsrc_t rA,
-                                            __amdgpu_buffer_rsrc_t rM, const char* B, int64_t btotal, int n0, int N,
-                                            int64_t rowA, int w, int ks, bool full) {
+__device__ __forceinline__ void issue_stage(const Stage& st, const LaneConsts& lc, i32x4 rA, i32x4 rM, const char* B,
+                                            int64_t btotal, int n0, int N, int64_t rowA, int w, int ks, bool full) {
   constexpr int KS = op_kstep(OP), ES = op_esize(OP);
   const int l = lane_id();
   if (full) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, st.a + (w * 4 + i) * 1024, 16, (int)lc.voA[i], ks * 64, 0, 0);
+      dma16_asm(rA, lds_addr(st.a + (w * 4 + i) * 1024), (uint32_t)((int)lc.voA[i]), (uint32_t)(ks * 64));
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (w * 4 + i) * 16 + (l >> 2);
       const int64_t col = (int64_t)ks * 64 + 16 * ((l & 3) ^ swzA(row));
       const uint32_t off = col < rowA ? lc.voA[i] + (uint32_t)(ks * 64) : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, st.a + (w * 4 + i) * 1024, 16, (int)off, 0, 0, 0);
+      dma16_asm(rA, lds_addr(st.a + (w * 4 + i) * 1024), (uint32_t)((int)off), (uint32_t)(0));
     }
   }
   const int64_t start = ((int64_t)ks * KS * N + n0) * ES;
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(B + start, btotal - start);
+  const i32x4 rB = make_rsrc4(B + start, btotal - start);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, st.b + (w * 8 + i) * 1024, 16, (int)lc.voB[i], 0, 0, 0);
+    dma16_asm(rB, lds_addr(st.b + (w * 8 + i) * 1024), (uint32_t)((int)lc.voB[i]), (uint32_t)(0));
   if constexpr (ES == 2) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (full) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rM, st.m + (w * 2 + i) * 256, 4, (int)lc.voM[i], ks * 8, 0, 0);
+        dma4_asm(rM, lds_addr(st.m + (w * 2 + i) * 256), (uint32_t)((int)lc.voM[i]), (uint32_t)(ks * 8));
       } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rM, st.m + (w * 2 + i) * 256, 4, (int)(lc.voM[i] + ks * 8), 0, 0,
-                                                 0);
+        dma4_asm(rM, lds_addr(st.m + (w * 2 + i) * 256), (uint32_t)((int)(lc.voM[i] + ks * 8)), (uint32_t)(0));
       }
     }
   } else {
-    if (full) __builtin_amdgcn_raw_ptr_buffer_load_lds(rM, st.m + w * 1024, 16, (int)lc.voM[0], ks * 16, 0, 0);
-    else __builtin_amdgcn_raw_ptr_buffer_load_lds(rM, st.m + w * 1024, 16, (int)(lc.voM[0] + ks * 16), 0, 0, 0);
+    if (full) dma16_asm(rM, lds_addr(st.m + w * 1024), (uint32_t)((int)lc.voM[0]), (uint32_t)(ks * 16));
+    else dma16_asm(rM, lds_addr(st.m + w * 1024), (uint32_t)((int)(lc.voM[0] + ks * 16)), (uint32_t)(0));
   }
 }
 
@@ -234,12 +234,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(const char* __r
                                                                   const char* __restrict__ B, void* C, int M, int N,
                                                                   int K, float alpha, float beta, int tiles_m,
                                                                   int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) char lA0[kLdsA], lA1[kLdsA], lA2[kLdsA];
-  __shared__ __attribute__((aligned(1024))) char lB0[kLdsB], lB1[kLdsB], lB2[kLdsB];
-  __shared__ __attribute__((aligned(1024))) char lM0[kLdsM], lM1[kLdsM], lM2[kLdsM];
-  const Stage s0{(SP24_LDS char*)lA0, (SP24_LDS char*)lB0, (SP24_LDS char*)lM0};
-  const Stage s1{(SP24_LDS char*)lA1, (SP24_LDS char*)lB1, (SP24_LDS char*)lM1};
-  const Stage s2{(SP24_LDS char*)lA2, (SP24_LDS char*)lB2, (SP24_LDS char*)lM2};
+  // One LDS object per stage (A | B | meta): the compiler's wait insertion
+  // tells direct-to-LDS loads apart only by the object they write, and it
+  // tracks only a few such objects.
+  __shared__ __attribute__((aligned(1024))) char lS0[kLdsStage], lS1[kLdsStage], lS2[kLdsStage];
+  const Stage s0 = stage_of((SP24_LDS char*)lS0);
+  const Stage s1 = stage_of((SP24_LDS char*)lS1);
+  const Stage s2 = stage_of((SP24_LDS char*)lS2);
   constexpr int KS = op_kstep(OP), ES = op_esize(OP);
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
@@ -262,8 +263,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(const char* __r
   const int64_t rowM = (int64_t)K / 8;       // bytes per metadata row
   const int ldb = N * ES;
   const LaneConsts lc = make_lane_consts<OP>(w, l, rowA, rowM, ldb);
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A_vals + (int64_t)m0 * rowA, (int64_t)(M - m0) * rowA);
-  const __amdgpu_buffer_rsrc_t rM = make_rsrc(meta + (int64_t)m0 * rowM, (int64_t)(M - m0) * rowM);
+  const i32x4 rA = make_rsrc4(A_vals + (int64_t)m0 * rowA, (int64_t)(M - m0) * rowA);
+  const i32x4 rM = make_rsrc4(meta + (int64_t)m0 * rowM, (int64_t)(M - m0) * rowM);
   const int64_t btotal = (int64_t)K * N * ES;
   const int nsteps = (K + KS - 1) / KS;
   const int nfull = K / KS;  // steps that lie wholly inside K
@@ -347,6 +348,266 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_large_kernel(const char* __r
           D[o] = beta != 0.0f ? v + D[o] : v;
         } else {
           // cast the whole vector: a bit cast of one vector element is not safe here
+          const f32x4 fv = __builtin_bit_cast(f32x4, acc[tm][tn]);
+          float* D = static_cast<float*>(C);
+          const float v = fv[r] * alpha;
+          D[o] = beta != 0.0f ? v + beta * D[o] : v;
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 8-wave variant of the large-tile kernel: the same 256 x 256 tile and A / B
+// LDS layout, but 8 waves (two per SIMD) in 2 x 4, each owning 128 x 64 =
+// 8 x 4 instruction tiles (128 accumulators).  With two waves per SIMD one
+// wave's LDS reads and barrier waits overlap the other wave's MFMAs.
+//
+// Global -> LDS staging:
+//   A, B   one k-step per stage, three stages (48 KiB each) in flight;
+//   meta   two k-steps per load (16 or 32 contiguous bytes per row instead
+//          of 8 or 16 -- the per-row pieces are what the loads pay for), in
+//          its own double buffer, issued together with the A / B data of the
+//          group's first step.
+// ----------------------------------------------------------------------------
+constexpr int kThreads8 = 512;
+constexpr int kLdsAB = kLdsA + kLdsB;        // 48 KiB per stage
+constexpr int kLdsMeta = kBM * 32;           // one metadata group, 8 KiB (16-bit inputs use half)
+
+struct LaneConsts8 {
+  uint32_t voA[2];
+  uint32_t voB[4];
+  uint32_t voM[2];
+  int ldsA;
+  int ldsM;
+  int ldsB[4];
+};
+
+// Metadata group: 2 k-steps.  LDS layout [row][group bytes]: 16 B per row for
+// 16-bit inputs (k-step j of the group at byte 8j), 32 B for 8-bit (16j).
+template <int OP>
+__host__ __device__ constexpr int meta_group_bytes() { return op_esize(OP) == 2 ? 16 : 32; }
+// DMA loads per wave per group: 16-bit inputs 2 x (16 rows x 16 B, 4 B per
+// lane); 8-bit inputs 1 x (32 rows x 32 B, 16 B per lane).
+template <int OP>
+__host__ __device__ constexpr int meta_loads8() { return op_esize(OP) == 2 ? 2 : 1; }
+
+template <int OP>
+__device__ __forceinline__ LaneConsts8 make_lane_consts8(int w, int l, int64_t rowA, int64_t rowM, int ldb) {
+  constexpr int ES = op_esize(OP);
+  LaneConsts8 c;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = (w * 2 + i) * 16 + (l >> 2);
+    c.voA[i] = (uint32_t)(row * rowA + 16 * ((l & 3) ^ swzA(row)));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = w * 4 + i;
+    int row, ch;
+    if constexpr (ES == 2) {
+      row = j * 2 + (l >> 5);
+      const int p = l & 31;
+      ch = (((p >> 1) ^ swzB16(row)) << 1) | (p & 1);
+    } else {
+      row = j * 4 + (l >> 4);
+      ch = (l & 15) ^ swzB8(row);
+    }
+    c.voB[i] = (uint32_t)(row * ldb + 16 * ch);
+  }
+  if constexpr (ES == 2) {
+    // 256 rows x 16 B = 4 KiB: two 4-byte loads per lane per wave (16 rows each)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) c.voM[i] = (uint32_t)(((w * 2 + i) * 16 + (l >> 2)) * rowM + 4 * (l & 3));
+  } else {
+    // 256 rows x 32 B = 8 KiB: one 16-byte load per lane per wave (32 rows)
+    c.voM[0] = (uint32_t)((w * 32 + (l >> 1)) * rowM + 16 * (l & 1));
+    c.voM[1] = 0;
+  }
+  const int wm = w >> 2, wn = w & 3, ga = l >> 4, r16 = l & 15;
+  c.ldsA = (wm * 128 + r16) * 64 + 16 * (ga ^ swzA(r16));
+  c.ldsM = (wm * 128 + r16) * meta_group_bytes<OP>() + (ES == 2 ? 2 * ga : 4 * ga);
+  const int gb = l >> 4, s = l & 15;
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn) {
+    const int ct = wn * 4 + tn;
+    if constexpr (ES == 2) {
+      const int k0 = 8 * gb + (s >> 2);
+      c.ldsB[tn] = k0 * 512 + ((ct ^ swzB16(k0)) << 5) + (s & 3) * 8;
+    } else {
+      const int k0 = 16 * gb + (s >> 1);
+      c.ldsB[tn] = k0 * 256 + ((ct ^ swzB8(k0)) << 4) + (s & 1) * 8;
+    }
+  }
+  return c;
+}
+
+constexpr int kLoadsAB8 = 2 + 4;  // A + B loads per wave per k-step
+
+// A and B of k-step ks into a stage.  `full`: the step lies wholly inside K
+// (the last step of a K that is not a multiple of KS masks A past the row end).
+template <int OP>
+__device__ __forceinline__ void issue_ab8(SP24_LDS char* st, const LaneConsts8& lc, i32x4 rA, const char* B,
+                                          int64_t btotal, int n0, int N, int64_t rowA, int w, int ks, bool full) {
+  constexpr int KS = op_kstep(OP), ES = op_esize(OP);
+  const int l = lane_id();
+  const uint32_t la = lds_addr(st);
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16_asm(rA, la + (w * 2 + i) * 1024, lc.voA[i], (uint32_t)(ks * 64));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = (w * 2 + i) * 16 + (l >> 2);
+      const int64_t col = (int64_t)ks * 64 + 16 * ((l & 3) ^ swzA(row));
+      const uint32_t off = col < rowA ? lc.voA[i] + (uint32_t)(ks * 64) : kOOB;
+      dma16_asm(rA, la + (w * 2 + i) * 1024, off, 0u);
+    }
+  }
+  const int64_t start = ((int64_t)ks * KS * N + n0) * ES;
+  const i32x4 rB = make_rsrc4(B + start, btotal - start);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dma16_asm(rB, la + kLdsA + (w * 4 + i) * 1024, lc.voB[i], 0u);
+}
+
+// Metadata group g (k-steps 2g, 2g+1) into a metadata buffer.  Rows past M and
+// bytes past the row end read as zero (range-checked loads; the zero codes
+// meet zero A values).
+template <int OP>
+__device__ __forceinline__ void issue_meta8(SP24_LDS char* mb, const LaneConsts8& lc, i32x4 rM, int64_t rowM, int w,
+                                            int g) {
+  constexpr int GB = meta_group_bytes<OP>();
+  const int l = lane_id();
+  const uint32_t la = lds_addr(mb);
+  if constexpr (op_esize(OP) == 2) {
+    const int64_t col = (int64_t)g * GB + 4 * (l & 3);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t off = col < rowM ? lc.voM[i] + (uint32_t)(g * GB) : kOOB;
+      dma4_asm(rM, la + (w * 2 + i) * 256, off, 0u);
+    }
+  } else {
+    const int64_t col = (int64_t)g * GB + 16 * (l & 1);
+    const uint32_t off = col < rowM ? lc.voM[0] + (uint32_t)(g * GB) : kOOB;
+    dma16_asm(rM, la + w * 1024, off, 0u);
+  }
+}
+
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() { waitcnt<VM, 0>(); }
+
+template <int OP>
+__global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __restrict__ A_vals,
+                                                                 const char* __restrict__ meta,
+                                                                 const char* __restrict__ B, void* C, int M, int N,
+                                                                 int K, float alpha, float beta, int tiles_m,
+                                                                 int tiles_n) {
+  // One LDS object per buffer.
+  __shared__ __attribute__((aligned(1024))) char lS0[kLdsAB], lS1[kLdsAB], lS2[kLdsAB];
+  __shared__ __attribute__((aligned(1024))) char lM0[kLdsMeta], lM1[kLdsMeta];
+  // (uniform selects; an array of LDS pointers would become a table in memory)
+  auto st = [&](int i) -> SP24_LDS char* {
+    return i == 0 ? (SP24_LDS char*)lS0 : (i == 1 ? (SP24_LDS char*)lS1 : (SP24_LDS char*)lS2);
+  };
+  auto mb = [&](int i) -> SP24_LDS char* { return i == 0 ? (SP24_LDS char*)lM0 : (SP24_LDS char*)lM1; };
+  constexpr int KS = op_kstep(OP), ES = op_esize(OP);
+  constexpr int LM = meta_loads8<OP>();
+
+  const int ntiles = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((ntiles & 7) == 0) t = (t & 7) * (ntiles >> 3) + (t >> 3);
+  constexpr int GM = 8;
+  const int group = t / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int in_group = t - group * GM * tiles_n;
+  const int m0 = (first_m + in_group % gsize) * kBM;
+  const int n0 = (in_group / gsize) * kBN;
+
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int l = lane_id();
+  const int64_t rowA = (int64_t)K / 2 * ES;
+  const int64_t rowM = (int64_t)K / 8;
+  const int ldb = N * ES;
+  const LaneConsts8 lc = make_lane_consts8<OP>(w, l, rowA, rowM, ldb);
+  const i32x4 rA = make_rsrc4(A_vals + (int64_t)m0 * rowA, (int64_t)(M - m0) * rowA);
+  const i32x4 rM = make_rsrc4(meta + (int64_t)m0 * rowM, (int64_t)(M - m0) * rowM);
+  const int64_t btotal = (int64_t)K * N * ES;
+  const int nsteps = (K + KS - 1) / KS;
+  const int nfull = K / KS;
+
+  i32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+  // DMA of step j: its metadata group first when j starts a group.
+  auto issue = [&](int j) {
+    if ((j & 1) == 0) issue_meta8<OP>(mb((j >> 1) & 1), lc, rM, rowM, w, j >> 1);
+    issue_ab8<OP>(st(j % 3), lc, rA, B, btotal, n0, N, rowA, w, j, j < nfull);
+  };
+  if (nsteps > 0) issue(0);
+  if (nsteps > 1) issue(1);
+  for (int ks = 0; ks < nsteps; ++ks) {
+    // Step ks's data is complete once only the loads of step ks+1 remain.
+    if (ks + 1 < nsteps) {
+      if (((ks + 1) & 1) == 0) wait_vm_lgkm0<kLoadsAB8 + LM>();
+      else wait_vm_lgkm0<kLoadsAB8>();
+    } else {
+      wait_vm_lgkm0<0>();
+    }
+    stage_barrier();
+    if (ks + 2 < nsteps) issue(ks + 2);
+    const SP24_LDS char* cur = st(ks % 3);
+    const SP24_LDS char* cm = mb((ks >> 1) & 1) + (ks & 1) * (meta_group_bytes<OP>() / 2);
+    i32x8 b[4];
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      const SP24_LDS char* p = cur + kLdsA + lc.ldsB[tn];
+      i32x2 q[4];
+      if constexpr (ES == 2) {
+        q[0] = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((SP24_LDS i16x4*)(p)));
+        q[1] = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((SP24_LDS i16x4*)(p + 2048)));
+        q[2] = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((SP24_LDS i16x4*)(p + 16384)));
+        q[3] = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((SP24_LDS i16x4*)(p + 18432)));
+      } else {
+        q[0] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SP24_LDS i32x2*)(p));
+        q[1] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SP24_LDS i32x2*)(p + 2048));
+        q[2] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SP24_LDS i32x2*)(p + 16384));
+        q[3] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SP24_LDS i32x2*)(p + 18432));
+      }
+      b[tn] = i32x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
+    }
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm) {
+      const i32x4 a = *(const SP24_LDS i32x4*)(cur + lc.ldsA + tm * 1024);
+      int idx;
+      if constexpr (ES == 2) idx = *(const SP24_LDS unsigned short*)(cm + lc.ldsM + tm * 16 * 16);
+      else idx = *(const SP24_LDS int*)(cm + lc.ldsM + tm * 16 * 32);
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = smfmac16<OP>(acc[tm][tn], a, b[tn], idx);
+    }
+  }
+
+  const int wm = w >> 2, wn = w & 3;
+#pragma unroll
+  for (int tm = 0; tm < 8; ++tm) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + wm * 128 + tm * 16 + 4 * (l >> 4) + r;
+      if (row >= M) continue;
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) {
+        const int col = n0 + wn * 64 + tn * 16 + (l & 15);
+        if (col >= N) continue;
+        const int64_t o = (int64_t)row * N + col;
+        if constexpr (op_is_int(OP)) {
+          int* D = static_cast<int*>(C);
+          const int v = acc[tm][tn][r];
+          D[o] = beta != 0.0f ? v + D[o] : v;
+        } else {
           const f32x4 fv = __builtin_bit_cast(f32x4, acc[tm][tn]);
           float* D = static_cast<float*>(C);
           const float v = fv[r] * alpha;
@@ -511,8 +772,13 @@ static hipError_t launch_op(const void* A_vals, const uint32_t* meta, const void
     return hipGetLastError();
   }
   const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+#ifdef SP24_LARGE4
   hipLaunchKernelGGL((gemm_large_kernel<OP>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0, stream, a, m, b,
                      C, M, N, K, alpha, beta, tiles_m, tiles_n);
+#else
+  hipLaunchKernelGGL((gemm_large8_kernel<OP>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads8), 0, stream, a, m,
+                     b, C, M, N, K, alpha, beta, tiles_m, tiles_n);
+#endif
   return hipGetLastError();
 }
 

@@ -80,6 +80,25 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, SP24_LDS void* ld
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 4, (int)voff, 0, 0, 0);
 }
 
+// The same direct-to-LDS loads issued through inline assembly.  The compiler
+// then does not see an LDS write, so it inserts no waits of its own for them
+// (its alias tracking for these loads is lost across branches and the loop
+// back-edge, which made it wait for every freshly issued load); callers wait
+// with explicit s_waitcnt vmcnt and order LDS reads with barriers that carry
+// a memory clobber.  The buffer resource is a plain SGPR quad.
+__device__ __forceinline__ i32x4 make_rsrc4(const void* base, uint64_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t n = (uint32_t)(bytes < kMaxRecords ? bytes : kMaxRecords);
+  return i32x4{(int)(uint32_t)b, (int)((b >> 32) & 0xFFFFu), (int)n, SP24_RSRC_WORD3};
+}
+__device__ __forceinline__ uint32_t lds_addr(const SP24_LDS void* p) { return (uint32_t)(uintptr_t)p; }
+__device__ __forceinline__ void dma16_asm(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds));
+}
+__device__ __forceinline__ void dma4_asm(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds));
+}
+
 // s_waitcnt with only vmcnt (and lgkmcnt) constrained (gfx9 encoding).
 template <int VM, int LGKM = 15>
 __device__ __forceinline__ void waitcnt() {
