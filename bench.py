@@ -112,6 +112,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="f16_8192", choices=sorted(WORKLOADS))
+    ap.add_argument("--layout", default="kblock", choices=["kblock", "row"],
+                    help="compressed layout the step writes and the GEMM reads")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the oracle sample (default: sized to ~15 s)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--gemm-only-launches", type=int, default=0,
@@ -145,19 +147,22 @@ def main():
     out_dtype = torch.int32 if w.a_type == wl.I8 else torch.float32
     C = torch.from_numpy(w.C).to(dev) if w.C is not None else torch.empty((w.M, w.N), dtype=out_dtype, device=dev)
     C0 = C.clone() if w.beta != 0.0 else None
-    vals = torch.empty((w.M, w.K // 2), dtype=A.dtype, device=dev)
-    meta = torch.empty((w.M, w.K // 32), dtype=torch.int32, device=dev)
+    layout = {"kblock": pkg.SP24_LAYOUT_KBLOCK, "row": pkg.SP24_LAYOUT_ROW}[args.layout]
+    vshape, mshape = pkg.compressed_shapes(w.M, w.K, w.a_type, layout)
+    vals = torch.empty(vshape, dtype=A.dtype, device=dev)
+    meta = torch.empty(mshape, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
     def compress():
-        st = pkg.sp24_prune_compress(A.data_ptr(), vals.data_ptr(), meta.data_ptr(), w.M, w.K, w.a_type, sh)
+        st = pkg.sp24_prune_compress(A.data_ptr(), vals.data_ptr(), meta.data_ptr(), w.M, w.K, w.a_type, layout,
+                                      sh)
         if st:
             raise pkg.Sp24Error(st, "sp24_prune_compress")
 
     def gemm():
-        st = pkg.sp24_gemm(vals.data_ptr(), meta.data_ptr(), w.a_type, B.data_ptr(), w.b_type, C.data_ptr(),
-                           w.M, w.N, w.K, w.alpha, w.beta, None, 0, sh)
+        st = pkg.sp24_gemm(vals.data_ptr(), meta.data_ptr(), w.a_type, layout, B.data_ptr(), w.b_type,
+                           C.data_ptr(), w.M, w.N, w.K, w.alpha, w.beta, None, 0, sh)
         if st:
             raise pkg.Sp24Error(st, "sp24_gemm")
 
@@ -199,9 +204,9 @@ def main():
     flop = 2.0 * w.M * w.N * w.K
     es_a = wl.ESIZE[w.a_type]
     es_b = wl.ESIZE[w.b_type]
-    comp_bytes = es_a * w.M * w.K + es_a * w.M * w.K // 2 + w.M * w.K // 8
-    gemm_bytes = es_a * w.M * w.K // 2 + w.M * w.K // 8 + es_b * w.K * w.N + 4 * w.M * w.N * (
-        2 if w.beta != 0.0 else 1)
+    cbytes = pkg.sp24_values_bytes(w.M, w.K, w.a_type, layout) + pkg.sp24_meta_bytes(w.M, w.K, w.a_type, layout)
+    comp_bytes = es_a * w.M * w.K + cbytes
+    gemm_bytes = cbytes + es_b * w.K * w.N + 4 * w.M * w.N * (2 if w.beta != 0.0 else 1)
     gemm_tflops = flop / (gemm_ms * 1e-3) / 1e12
     comp_gbps = comp_bytes / (comp_ms * 1e-3) / 1e9
     gemm_gbps = gemm_bytes / (gemm_ms * 1e-3) / 1e9
@@ -234,7 +239,7 @@ def main():
         else "i8->i32",
         "data": "synthetic",
         "config": {"workload": args.workload, "M": w.M, "N": w.N, "K": w.K, "a_type": wl_name(w.a_type),
-                   "b_type": wl_name(w.b_type), "alpha": w.alpha, "beta": w.beta,
+                   "b_type": wl_name(w.b_type), "alpha": w.alpha, "beta": w.beta, "layout": args.layout,
                    "step": "sp24_prune_compress(A) + sp24_gemm(A_vals, meta, B, C)"},
         "gemm_tflops": round(gemm_tflops, 1),
         "gemm_frac_sparse_peak": round(gemm_tflops / PEAK_SPARSE_TFLOPS[label], 4),

@@ -13,16 +13,29 @@
  *   D = alpha * expand(A_vals, meta) * B + beta * C, accumulated in fp32
  *   (int32 for int8).
  *
- * Layouts (all row-major, dense leading dimensions, no padding):
+ * Dense layouts (row-major, dense leading dimensions, no padding):
  *   A       M x K elements of the input type, K contiguous.
- *   A_vals  M x K/2 elements of the same type.
- *   meta    M x K/32 uint32 words.  The code (0..3, position inside its group
- *           of 4) of compressed element c of row i is held in bits
- *           [2*(c%16), 2*(c%16)+1] of meta[i*(K/32) + c/16].  With the
- *           positions-0-and-2 pattern every byte reads 0x88, the index value
- *           the pages' CDNA examples pass to the instruction.
  *   B       K x N elements, N contiguous.  K is the dense K.
  *   C / D   M x N float32 (int32 when both inputs are int8), updated in place.
+ *
+ * Compressed layouts (sp24_layout).  In both, the 2-bit code (0..3, position
+ * inside its group of 4) of compressed element c of a row sits at bits
+ * [2*(c%16), 2*(c%16)+1] of that row's metadata word c/16 (LSB first; with
+ * the positions-0-and-2 pattern every byte reads 0x88, the index value the
+ * pages' CDNA examples pass to the instruction).
+ *   SP24_LAYOUT_ROW     A_vals is M x K/2 elements, row-major; meta is
+ *                       M x K/32 uint32 words, row-major.  The reference
+ *                       layout.
+ *   SP24_LAYOUT_KBLOCK  GEMM-ready: K is cut into blocks of KB dense columns
+ *                       (KB = 64 for 16-bit types, 128 for 8-bit types; each
+ *                       block is 64 bytes of compressed values per row), and
+ *                       block b of all M rows is stored together:
+ *                         A_vals bytes [(b*M + i)*64, +64) = row i, block b;
+ *                         meta words   [(b*M + i)*W, +W)   = row i, block b,
+ *                       with W = KB/32 words (2 or 4).  ceil(K/KB) blocks;
+ *                       the tail of a last partial block is zero.  One
+ *                       k-step of a 256-row tile is then a single contiguous
+ *                       16 KiB run of values and 2 or 4 KiB of metadata.
  *
  * Element types (sp24_dtype): fp16 (IEEE binary16), bf16, int8 (two's
  * complement), fp8 E4M3 and bf8 E5M2 (both OCP: E4M3 has no infinities and
@@ -60,6 +73,11 @@ typedef enum {
 } sp24_dtype;
 
 typedef enum {
+  SP24_LAYOUT_ROW = 0,
+  SP24_LAYOUT_KBLOCK = 1
+} sp24_layout;
+
+typedef enum {
   SP24_OK = 0,
   SP24_ERR_INVALID_VALUE = 1, /* bad shape, null pointer, overlap, workspace too small */
   SP24_ERR_UNSUPPORTED = 2,   /* type pair, alpha/beta or leading dimension not supported */
@@ -67,12 +85,13 @@ typedef enum {
   SP24_ERR_LAUNCH = 4         /* the HIP runtime refused the kernel launch */
 } sp24_status;
 
-/* Bytes of A_vals for an M x K matrix of `dtype`: M * (K/2) * element size.
- * Returns 0 for an unknown dtype or negative sizes. */
-size_t sp24_values_bytes(int64_t M, int64_t K, int dtype);
+/* Bytes of A_vals for an M x K matrix of `dtype` in `layout`:
+ * ROW: M * (K/2) * element size; KBLOCK: ceil(K/KB) * M * 64.
+ * Returns 0 for an unknown dtype or layout or negative sizes. */
+size_t sp24_values_bytes(int64_t M, int64_t K, int dtype, int layout);
 
-/* Bytes of the metadata for an M x K matrix: M * (K/32) * 4. */
-size_t sp24_meta_bytes(int64_t M, int64_t K);
+/* Bytes of the metadata: ROW: M * (K/32) * 4; KBLOCK: ceil(K/KB) * M * KB/8. */
+size_t sp24_meta_bytes(int64_t M, int64_t K, int dtype, int layout);
 
 /* Workspace that sp24_gemm needs for this problem (currently always 0: the
  * kernels reduce split-K partial sums on chip). */
@@ -92,14 +111,15 @@ size_t sp24_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int a_type, in
  * 2:4 is therefore compressed losslessly.
  *
  *   A       in:  M x K elements of `dtype`.
- *   A_vals  out: M x K/2 elements (sp24_values_bytes).
- *   meta    out: M x K/32 words (sp24_meta_bytes).
+ *   A_vals  out: sp24_values_bytes(M, K, dtype, layout) bytes.
+ *   meta    out: sp24_meta_bytes(M, K, dtype, layout) bytes.
  *   M, K    M >= 0, K >= 0, K % 32 == 0.  M == 0 or K == 0 enqueues nothing.
+ *   layout  SP24_LAYOUT_ROW or SP24_LAYOUT_KBLOCK.
  * Errors: INVALID_VALUE (shape, null pointer with nonzero size, A overlapping
- * an output), UNSUPPORTED (unknown dtype), MISALIGNED (pointer not 16-byte
- * aligned), LAUNCH.
+ * an output), UNSUPPORTED (unknown dtype or layout), MISALIGNED (pointer not
+ * 16-byte aligned), LAUNCH.
  */
-int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, int64_t K, int dtype,
+int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, int64_t K, int dtype, int layout,
                         void* stream);
 
 /*
@@ -111,23 +131,27 @@ int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, 
  * page: "D = A (sparse) * B + D").  Products of the supported inputs are
  * exact in fp32; sums are fp32 (exact int32 for int8).
  *
- *   A_vals, meta  compressed A as produced by sp24_prune_compress (or any
- *                 caller-built data in the same layout; codes are trusted --
- *                 a group whose two codes are not strictly increasing gives
- *                 unspecified results).
+ *   A_vals, meta  compressed A in `layout`, as produced by
+ *                 sp24_prune_compress (or any caller-built data in the same
+ *                 layout; codes are trusted -- a group whose two codes are
+ *                 not strictly increasing gives unspecified results).
  *   a_type        element type of A_vals; b_type element type of B.
  *   B             K x N elements of b_type.
  *   C             in/out: M x N float32 (int32 for int8 x int8).  Not read
  *                 when beta == 0 (NaN there does not propagate).
- *   M, N, K       >= 0, K % 32 == 0, N * sizeof(b_type) % 16 == 0.
+ *   M, N, K       >= 0, K % 32 == 0, N * sizeof(b_type) % 16 == 0,
+ *                 N * sizeof(b_type) <= 16 MiB - 2 (so 128 rows of B stay
+ *                 below 2 GiB) and, for the ROW layout, 256 * K/2 *
+ *                 sizeof(a_type) < 2 GiB (K <= 8388606 for 16-bit types).
  *                 M == 0 or N == 0: nothing is enqueued.  K == 0: D = beta*C.
  *   alpha, beta   float scalars.  For int8: alpha must be 1, beta 0 or 1.
  *   workspace     may be NULL when sp24_gemm_workspace_bytes() == 0.
  * Errors: INVALID_VALUE (shape, null pointer, C overlapping an input,
  * workspace too small), UNSUPPORTED (type pair, int8 alpha/beta, N*size not a
- * multiple of 16 bytes), MISALIGNED, LAUNCH.
+ * multiple of 16 bytes, N or K past the limits above, unknown layout),
+ * MISALIGNED, LAUNCH.
  */
-int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, const void* B, int b_type, void* C,
+int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, const void* B, int b_type, void* C,
               int64_t M, int64_t N, int64_t K, float alpha, float beta, void* workspace,
               size_t workspace_bytes, void* stream);
 

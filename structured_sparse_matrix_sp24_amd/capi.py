@@ -16,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsp24.so")
 
 SP24_F16, SP24_BF16, SP24_I8, SP24_FP8_E4M3, SP24_BF8_E5M2 = 1, 2, 3, 4, 5
+SP24_LAYOUT_ROW, SP24_LAYOUT_KBLOCK = 0, 1
 SP24_OK = 0
 _ESIZE = {SP24_F16: 2, SP24_BF16: 2, SP24_I8: 1, SP24_FP8_E4M3: 1, SP24_BF8_E5M2: 1}
 
@@ -36,15 +37,15 @@ def lib():
             raise ImportError(f"libsp24.so not built ({LIB_PATH}); run __graft_entry__.build()")
         L = ctypes.CDLL(LIB_PATH)
         P, I64, I, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-        L.sp24_values_bytes.argtypes = [I64, I64, I]
+        L.sp24_values_bytes.argtypes = [I64, I64, I, I]
         L.sp24_values_bytes.restype = SZ
-        L.sp24_meta_bytes.argtypes = [I64, I64]
+        L.sp24_meta_bytes.argtypes = [I64, I64, I, I]
         L.sp24_meta_bytes.restype = SZ
         L.sp24_gemm_workspace_bytes.argtypes = [I64, I64, I64, I, I]
         L.sp24_gemm_workspace_bytes.restype = SZ
-        L.sp24_prune_compress.argtypes = [P, P, P, I64, I64, I, P]
+        L.sp24_prune_compress.argtypes = [P, P, P, I64, I64, I, I, P]
         L.sp24_prune_compress.restype = I
-        L.sp24_gemm.argtypes = [P, P, I, P, I, P, I64, I64, I64, F, F, P, SZ, P]
+        L.sp24_gemm.argtypes = [P, P, I, I, P, I, P, I64, I64, I64, F, F, P, SZ, P]
         L.sp24_gemm.restype = I
         L.sp24_status_string.argtypes = [I]
         L.sp24_status_string.restype = ctypes.c_char_p
@@ -55,26 +56,28 @@ def lib():
 
 
 # ---- one-to-one C ABI mirrors ------------------------------------------------
-def sp24_values_bytes(M: int, K: int, dtype: int) -> int:
-    return lib().sp24_values_bytes(M, K, dtype)
+def sp24_values_bytes(M: int, K: int, dtype: int, layout: int) -> int:
+    return lib().sp24_values_bytes(M, K, dtype, layout)
 
 
-def sp24_meta_bytes(M: int, K: int) -> int:
-    return lib().sp24_meta_bytes(M, K)
+def sp24_meta_bytes(M: int, K: int, dtype: int, layout: int) -> int:
+    return lib().sp24_meta_bytes(M, K, dtype, layout)
 
 
 def sp24_gemm_workspace_bytes(M: int, N: int, K: int, a_type: int, b_type: int) -> int:
     return lib().sp24_gemm_workspace_bytes(M, N, K, a_type, b_type)
 
 
-def sp24_prune_compress(A: int, A_vals: int, meta: int, M: int, K: int, dtype: int, stream: int | None) -> int:
-    return lib().sp24_prune_compress(A, A_vals, meta, M, K, dtype, stream)
+def sp24_prune_compress(A: int, A_vals: int, meta: int, M: int, K: int, dtype: int, layout: int,
+                        stream: int | None) -> int:
+    return lib().sp24_prune_compress(A, A_vals, meta, M, K, dtype, layout, stream)
 
 
-def sp24_gemm(A_vals: int, meta: int, a_type: int, B: int, b_type: int, C: int, M: int, N: int, K: int,
-              alpha: float, beta: float, workspace: int | None, workspace_bytes: int, stream: int | None) -> int:
-    return lib().sp24_gemm(A_vals, meta, a_type, B, b_type, C, M, N, K, alpha, beta, workspace, workspace_bytes,
-                           stream)
+def sp24_gemm(A_vals: int, meta: int, a_type: int, layout: int, B: int, b_type: int, C: int, M: int, N: int,
+              K: int, alpha: float, beta: float, workspace: int | None, workspace_bytes: int,
+              stream: int | None) -> int:
+    return lib().sp24_gemm(A_vals, meta, a_type, layout, B, b_type, C, M, N, K, alpha, beta, workspace,
+                           workspace_bytes, stream)
 
 
 def sp24_status_string(status: int) -> str:
@@ -107,37 +110,63 @@ def _stream(stream=None):
     return s.cuda_stream
 
 
-def prune_compress(A, dtype: int | None = None, stream=None):
+def kblock_width(dtype: int) -> int:
+    """Dense K columns per block of the K-blocked layout: 64 (16-bit types) or 128 (8-bit)."""
+    return 64 if _ESIZE[dtype] == 2 else 128
+
+
+def compressed_shapes(M: int, K: int, dtype: int, layout: int):
+    """Tensor shapes (values in elements of ``dtype``, metadata in 32-bit words)
+    of a compressed M x K matrix in ``layout``."""
+    if layout == SP24_LAYOUT_ROW:
+        return (M, K // 2), (M, K // 32)
+    if layout == SP24_LAYOUT_KBLOCK:
+        kb = kblock_width(dtype)
+        nblk = -(-K // kb)
+        return (nblk, M, kb // 2), (nblk, M, kb // 32)
+    raise ValueError(f"unknown layout {layout}")
+
+
+def prune_compress(A, dtype: int | None = None, layout: int = SP24_LAYOUT_KBLOCK, stream=None):
     """A: M x K device tensor (any 1- or 2-byte dtype holding the bits of
-    ``dtype``).  Returns (A_vals M x K/2 uint8/int16 view-compatible tensor
-    of the same element size, meta M x K/32 int32 tensor holding uint32 words)."""
+    ``dtype``).  Returns (A_vals, meta) in ``layout``: ROW gives M x K/2 values
+    and M x K/32 metadata words; KBLOCK gives nblk x M x KB/2 values and
+    nblk x M x KB/32 words (KB = kblock_width(dtype)).  Metadata words are
+    uint32 held in int32 tensors."""
     import torch
     if dtype is None:
         dtype = dtype_code(A.dtype)
     if A.dim() != 2 or not A.is_contiguous():
         raise ValueError("A must be a contiguous 2-D tensor")
     M, K = A.shape
-    vals = torch.empty((M, K // 2), dtype=A.dtype, device=A.device)
-    meta = torch.empty((M, K // 32), dtype=torch.int32, device=A.device)
-    st = sp24_prune_compress(A.data_ptr(), vals.data_ptr(), meta.data_ptr(), M, K, dtype, _stream(stream))
+    vshape, mshape = compressed_shapes(M, K, dtype, layout)
+    vals = torch.empty(vshape, dtype=A.dtype, device=A.device)
+    meta = torch.empty(mshape, dtype=torch.int32, device=A.device)
+    st = sp24_prune_compress(A.data_ptr(), vals.data_ptr(), meta.data_ptr(), M, K, dtype, layout, _stream(stream))
     if st != SP24_OK:
         raise Sp24Error(st, "sp24_prune_compress")
     return vals, meta
 
 
 def gemm(A_vals, meta, B, C=None, alpha: float = 1.0, beta: float = 0.0, a_type: int | None = None,
-         b_type: int | None = None, stream=None):
-    """D = alpha * expand(A_vals, meta) @ B + beta * C, written into C (allocated
-    as zeros-free empty when C is None and beta == 0).  Returns C."""
+         b_type: int | None = None, layout: int | None = None, stream=None):
+    """D = alpha * expand(A_vals, meta) @ B + beta * C, written into C
+    (allocated, uninitialised, when C is None and beta == 0).  ``layout``
+    defaults to what the tensors' rank says: 2-D = ROW, 3-D = KBLOCK.
+    Returns C."""
     import torch
     if a_type is None:
         a_type = dtype_code(A_vals.dtype)
     if b_type is None:
         b_type = dtype_code(B.dtype)
-    M, KC = A_vals.shape
+    if layout is None:
+        layout = SP24_LAYOUT_KBLOCK if A_vals.dim() == 3 else SP24_LAYOUT_ROW
     K, N = B.shape
-    if K != 2 * KC:
-        raise ValueError(f"K mismatch: A_vals has {KC} compressed columns, B has {K} rows")
+    M = A_vals.shape[0] if layout == SP24_LAYOUT_ROW else A_vals.shape[1]
+    vshape, mshape = compressed_shapes(M, K, a_type, layout)
+    if tuple(A_vals.shape) != vshape or tuple(meta.shape) != mshape:
+        raise ValueError(f"compressed A has shapes {tuple(A_vals.shape)} / {tuple(meta.shape)}; "
+                         f"K = {K} in this layout needs {vshape} / {mshape}")
     out_dtype = torch.int32 if (a_type == SP24_I8 and b_type == SP24_I8) else torch.float32
     if C is None:
         if beta != 0.0:
@@ -146,7 +175,7 @@ def gemm(A_vals, meta, B, C=None, alpha: float = 1.0, beta: float = 0.0, a_type:
     for t in (A_vals, meta, B, C):
         if not t.is_contiguous():
             raise ValueError("all operands must be contiguous")
-    st = sp24_gemm(A_vals.data_ptr(), meta.data_ptr(), a_type, B.data_ptr(), b_type, C.data_ptr(), M, N, K,
+    st = sp24_gemm(A_vals.data_ptr(), meta.data_ptr(), a_type, layout, B.data_ptr(), b_type, C.data_ptr(), M, N, K,
                    float(alpha), float(beta), None, 0, _stream(stream))
     if st != SP24_OK:
         raise Sp24Error(st, "sp24_gemm")

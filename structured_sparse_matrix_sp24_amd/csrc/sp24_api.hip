@@ -6,9 +6,9 @@
 
 namespace sp24 {
 hipError_t launch_prune_compress(const void* A, void* vals, uint32_t* meta, int64_t M, int64_t K, int dtype,
-                                 hipStream_t stream);
-hipError_t launch_gemm(int op, const void* A_vals, const uint32_t* meta, const void* B, void* C, int M, int N, int K,
-                       float alpha, float beta, hipStream_t stream);
+                                 int layout, hipStream_t stream);
+hipError_t launch_gemm(int op, int layout, const void* A_vals, const uint32_t* meta, const void* B, void* C, int M,
+                       int N, int K, float alpha, float beta, hipStream_t stream);
 }  // namespace sp24
 
 namespace {
@@ -44,51 +44,68 @@ int op_for(int a, int b) {
 }
 
 constexpr int64_t kMaxDim = 0x7FFFFFFF;
+constexpr uint64_t kTileBytesMax = 0x7FFFFF00ull;
+
+bool layout_ok(int layout) { return layout == SP24_LAYOUT_ROW || layout == SP24_LAYOUT_KBLOCK; }
+
+// K-blocks of the GEMM-ready layout: 64 dense columns (16-bit) or 128 (8-bit).
+int64_t kblocks(int64_t K, int es) {
+  const int64_t kb = es == 2 ? 64 : 128;
+  return (K + kb - 1) / kb;
+}
 
 }  // namespace
 
 extern "C" {
 
-size_t sp24_values_bytes(int64_t M, int64_t K, int dtype) {
+size_t sp24_values_bytes(int64_t M, int64_t K, int dtype, int layout) {
   const int es = esize(dtype);
-  if (es == 0 || M < 0 || K < 0) return 0;
+  if (es == 0 || M < 0 || K < 0 || !layout_ok(layout)) return 0;
+  if (layout == SP24_LAYOUT_KBLOCK) return (size_t)kblocks(K, es) * (size_t)M * 64u;
   return (size_t)M * (size_t)(K / 2) * (size_t)es;
 }
 
-size_t sp24_meta_bytes(int64_t M, int64_t K) {
-  if (M < 0 || K < 0) return 0;
+size_t sp24_meta_bytes(int64_t M, int64_t K, int dtype, int layout) {
+  const int es = esize(dtype);
+  if (es == 0 || M < 0 || K < 0 || !layout_ok(layout)) return 0;
+  if (layout == SP24_LAYOUT_KBLOCK) return (size_t)kblocks(K, es) * (size_t)M * (es == 2 ? 8u : 16u);
   return (size_t)M * (size_t)(K / 32) * 4u;
 }
 
 size_t sp24_gemm_workspace_bytes(int64_t, int64_t, int64_t, int, int) { return 0; }
 
-int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, int64_t K, int dtype,
+int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, int64_t K, int dtype, int layout,
                         void* stream) {
   const int es = esize(dtype);
-  if (es == 0) return SP24_ERR_UNSUPPORTED;
+  if (es == 0 || !layout_ok(layout)) return SP24_ERR_UNSUPPORTED;
   if (M < 0 || K < 0 || K % 32 != 0 || M > kMaxDim || K > kMaxDim) return SP24_ERR_INVALID_VALUE;
   if (M == 0 || K == 0) return SP24_OK;
   if (!A || !A_vals || !meta) return SP24_ERR_INVALID_VALUE;
   if (!aligned16(A) || !aligned16(A_vals) || !aligned16(meta)) return SP24_ERR_MISALIGNED;
   const uint64_t a_bytes = (uint64_t)M * K * es;
-  const uint64_t v_bytes = sp24_values_bytes(M, K, dtype), m_bytes = sp24_meta_bytes(M, K);
+  const uint64_t v_bytes = sp24_values_bytes(M, K, dtype, layout), m_bytes = sp24_meta_bytes(M, K, dtype, layout);
   if (overlap(A, a_bytes, A_vals, v_bytes) || overlap(A, a_bytes, meta, m_bytes) ||
       overlap(A_vals, v_bytes, meta, m_bytes))
     return SP24_ERR_INVALID_VALUE;
   const hipError_t e =
-      sp24::launch_prune_compress(A, A_vals, meta, M, K, dtype, static_cast<hipStream_t>(stream));
+      sp24::launch_prune_compress(A, A_vals, meta, M, K, dtype, layout, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SP24_OK : SP24_ERR_LAUNCH;
 }
 
-int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, const void* B, int b_type, void* C, int64_t M,
-              int64_t N, int64_t K, float alpha, float beta, void* workspace, size_t workspace_bytes,
+int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, const void* B, int b_type, void* C,
+              int64_t M, int64_t N, int64_t K, float alpha, float beta, void* workspace, size_t workspace_bytes,
               void* stream) {
   const int op = op_for(a_type, b_type);
-  if (op < 0) return SP24_ERR_UNSUPPORTED;
+  if (op < 0 || !layout_ok(layout)) return SP24_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
     return SP24_ERR_INVALID_VALUE;
   const int ea = esize(a_type), eb = esize(b_type);
   if (((uint64_t)N * eb) % 16 != 0) return SP24_ERR_UNSUPPORTED;
+  // The kernels address one k-step of B (<= 128 rows) and, in the ROW layout,
+  // the compressed rows of one 256-row tile with 32-bit offsets inside
+  // buffer ranges below 2 GiB.
+  if ((uint64_t)N * eb * 128 > kTileBytesMax) return SP24_ERR_UNSUPPORTED;
+  if (layout == SP24_LAYOUT_ROW && (uint64_t)(K / 2) * ea * 256 > kTileBytesMax) return SP24_ERR_UNSUPPORTED;
   if (op == sp24::OP_I8 && (alpha != 1.0f || (beta != 0.0f && beta != 1.0f))) return SP24_ERR_UNSUPPORTED;
   if (workspace_bytes < sp24_gemm_workspace_bytes(M, N, K, a_type, b_type)) return SP24_ERR_INVALID_VALUE;
   (void)workspace;
@@ -98,10 +115,11 @@ int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, const void* 
   if (!aligned16(C) || (K > 0 && (!aligned16(A_vals) || !aligned16(meta) || !aligned16(B))))
     return SP24_ERR_MISALIGNED;
   const uint64_t c_bytes = (uint64_t)M * N * 4;
-  if (K > 0 && (overlap(C, c_bytes, A_vals, (uint64_t)M * (K / 2) * ea) ||
-                overlap(C, c_bytes, meta, (uint64_t)M * (K / 32) * 4) || overlap(C, c_bytes, B, (uint64_t)K * N * eb)))
+  if (K > 0 && (overlap(C, c_bytes, A_vals, sp24_values_bytes(M, K, a_type, layout)) ||
+                overlap(C, c_bytes, meta, sp24_meta_bytes(M, K, a_type, layout)) ||
+                overlap(C, c_bytes, B, (uint64_t)K * N * eb)))
     return SP24_ERR_INVALID_VALUE;
-  const hipError_t e = sp24::launch_gemm(op, A_vals, meta, B, C, (int)M, (int)N, (int)K, alpha, beta,
+  const hipError_t e = sp24::launch_gemm(op, layout, A_vals, meta, B, C, (int)M, (int)N, (int)K, alpha, beta,
                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SP24_OK : SP24_ERR_LAUNCH;
 }
@@ -117,6 +135,6 @@ const char* sp24_status_string(int status) {
   }
 }
 
-int sp24_version(void) { return 100; }
+int sp24_version(void) { return 200; }
 
 }  // extern "C"

@@ -14,6 +14,13 @@
 // whole 16-byte chunks with consecutive lanes on consecutive chunks, so every
 // wave instruction (load and store) is one contiguous span.  No MFMA, no LDS:
 // the kernel is bound by HBM bandwidth.
+//
+// The K-blocked output layout (one k-step of the GEMM = KB dense columns per
+// block, all M rows of a block stored together) uses a 2-D mapping instead:
+// a lane owns one 16-byte chunk of one row's block (8 chunks per block), so
+// eight consecutive lanes read one row's 128 contiguous bytes and a wave
+// writes eight consecutive rows of a block, i.e. one contiguous 512-byte run
+// of values and one 64- or 128-byte run of metadata.
 #include "sp24_internal.hpp"
 
 namespace sp24 {
@@ -112,21 +119,103 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kernel(const 
   }
 }
 
+// K-blocked layout.  Workgroup (row tile rt, block b) covers rows
+// rt*128 .. +128 of block b; thread t handles chunk t%8 of rows
+// rt*128 + t/8 + 32u (u < 4).  Consecutive workgroups take consecutive row
+// tiles of the same block, so the outputs of neighbouring workgroups are
+// neighbours in memory.  Chunks past K (the tail of a partial last block)
+// are written as zero values with zero codes.
+constexpr int kKbRowsPerTile = 128;
+
+template <int ES, bool INT>
+__global__ __launch_bounds__(kCompressThreads) void prune_compress_kblock_kernel(const char* __restrict__ A,
+                                                                                   char* __restrict__ vals,
+                                                                                   char* __restrict__ meta,
+                                                                                   int64_t M, int64_t K,
+                                                                                   uint32_t row_tiles) {
+  constexpr int MB = ES == 2 ? 8 : 16;         // metadata bytes per row per block
+  constexpr int CE = 16 / ES;                   // dense elements per chunk
+  const uint32_t rt = blockIdx.x % row_tiles;
+  const int64_t b = blockIdx.x / row_tiles;
+  const int c = threadIdx.x & 7;
+  const int64_t kcol = b * (8 * CE) + (int64_t)c * CE;  // first dense column of the chunk
+  const bool inside = kcol < K;
+  const int64_t rowbytes = K * ES;
+  i32x4 in[kCompressUnroll];
+#pragma unroll
+  for (int u = 0; u < kCompressUnroll; ++u) {
+    const int64_t row = (int64_t)rt * kKbRowsPerTile + (threadIdx.x >> 3) + 32 * u;
+    in[u] = i32x4{0, 0, 0, 0};
+    if (row < M && inside)
+      in[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(A + row * rowbytes + kcol * ES));
+  }
+#pragma unroll
+  for (int u = 0; u < kCompressUnroll; ++u) {
+    const int64_t row = (int64_t)rt * kKbRowsPerTile + (threadIdx.x >> 3) + 32 * u;
+    if (row >= M) break;
+    const int64_t slot = b * M + row;
+    const uint32_t d0 = (uint32_t)in[u][0], d1 = (uint32_t)in[u][1];
+    const uint32_t d2 = (uint32_t)in[u][2], d3 = (uint32_t)in[u][3];
+    i32x2 out = {0, 0};
+    i32x2* vp = reinterpret_cast<i32x2*>(vals + slot * 64 + c * 8);
+    if constexpr (ES == 2) {
+      uint8_t code = 0;
+      if (inside) {
+        uint32_t n0, n1;
+        out[0] = (int)group16((uint64_t)d0 | ((uint64_t)d1 << 32), n0);
+        out[1] = (int)group16((uint64_t)d2 | ((uint64_t)d3 << 32), n1);
+        code = (uint8_t)(n0 | (n1 << 4));
+      }
+      __builtin_nontemporal_store(out, vp);
+      __builtin_nontemporal_store(code, reinterpret_cast<uint8_t*>(meta + slot * MB + c));
+    } else {
+      uint16_t code = 0;
+      if (inside) {
+        uint32_t n0, n1, n2, n3;
+        const uint32_t v0 = group8<INT>(d0, n0), v1 = group8<INT>(d1, n1);
+        const uint32_t v2 = group8<INT>(d2, n2), v3 = group8<INT>(d3, n3);
+        out[0] = (int)(v0 | (v1 << 16));
+        out[1] = (int)(v2 | (v3 << 16));
+        code = (uint16_t)(n0 | (n1 << 4) | (n2 << 8) | (n3 << 12));
+      }
+      __builtin_nontemporal_store(out, vp);
+      __builtin_nontemporal_store(code, reinterpret_cast<uint16_t*>(meta + slot * MB + 2 * c));
+    }
+  }
+}
+
 // Host launcher (arguments already validated).
 hipError_t launch_prune_compress(const void* A, void* vals, uint32_t* meta, int64_t M, int64_t K, int dtype,
-                                 hipStream_t stream) {
+                                 int layout, hipStream_t stream) {
   const int es = (dtype == SP24_F16 || dtype == SP24_BF16) ? 2 : 1;
+  const bool is_int = dtype == SP24_I8;
+  if (M == 0 || K == 0) return hipSuccess;
+  const dim3 block(kCompressThreads);
+  if (layout == SP24_LAYOUT_KBLOCK) {
+    const int64_t kb = es == 2 ? 64 : 128;
+    const int64_t nblk = (K + kb - 1) / kb;
+    const int64_t row_tiles = (M + kKbRowsPerTile - 1) / kKbRowsPerTile;
+    if (row_tiles * nblk > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(row_tiles * nblk));
+    const char* a = static_cast<const char*>(A);
+    char* v = static_cast<char*>(vals);
+    char* m = reinterpret_cast<char*>(meta);
+    const uint32_t rt = (uint32_t)row_tiles;
+    if (es == 2) hipLaunchKernelGGL((prune_compress_kblock_kernel<2, false>), grid, block, 0, stream, a, v, m, M, K, rt);
+    else if (is_int) hipLaunchKernelGGL((prune_compress_kblock_kernel<1, true>), grid, block, 0, stream, a, v, m, M, K, rt);
+    else hipLaunchKernelGGL((prune_compress_kblock_kernel<1, false>), grid, block, 0, stream, a, v, m, M, K, rt);
+    return hipGetLastError();
+  }
   const int64_t nchunks = M * K * es / 16;
-  if (nchunks == 0) return hipSuccess;
   const int64_t per_block = (int64_t)kCompressThreads * kCompressUnroll;
   const int64_t blocks = (nchunks + per_block - 1) / per_block;
   if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(kCompressThreads);
+  const dim3 grid((unsigned)blocks);
   const i32x4* a = static_cast<const i32x4*>(A);
   i32x2* v = static_cast<i32x2*>(vals);
   uint8_t* m = reinterpret_cast<uint8_t*>(meta);
   if (es == 2) hipLaunchKernelGGL((prune_compress_kernel<2, false>), grid, block, 0, stream, a, v, m, nchunks);
-  else if (dtype == SP24_I8) hipLaunchKernelGGL((prune_compress_kernel<1, true>), grid, block, 0, stream, a, v, m, nchunks);
+  else if (is_int) hipLaunchKernelGGL((prune_compress_kernel<1, true>), grid, block, 0, stream, a, v, m, nchunks);
   else hipLaunchKernelGGL((prune_compress_kernel<1, false>), grid, block, 0, stream, a, v, m, nchunks);
   return hipGetLastError();
 }

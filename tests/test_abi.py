@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -33,12 +34,31 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_size_queries(L):
-    assert L.sp24_values_bytes(8192, 8192, L.SP24_F16) == 8192 * 4096 * 2
-    assert L.sp24_values_bytes(8192, 16384, L.SP24_FP8_E4M3) == 8192 * 8192
-    assert L.sp24_meta_bytes(8192, 8192) == 8192 * 8192 // 8
-    assert L.sp24_values_bytes(4, 64, 99) == 0
+    ROW, KB = L.SP24_LAYOUT_ROW, L.SP24_LAYOUT_KBLOCK
+    assert L.sp24_values_bytes(8192, 8192, L.SP24_F16, ROW) == 8192 * 4096 * 2
+    assert L.sp24_values_bytes(8192, 16384, L.SP24_FP8_E4M3, ROW) == 8192 * 8192
+    assert L.sp24_meta_bytes(8192, 8192, L.SP24_F16, ROW) == 8192 * 8192 // 8
+    # K-blocked: whole blocks of 64 B values and 8 / 16 B metadata per row
+    assert L.sp24_values_bytes(8192, 8192, L.SP24_F16, KB) == 8192 * 4096 * 2
+    assert L.sp24_meta_bytes(8192, 8192, L.SP24_F16, KB) == 8192 * 8192 // 8
+    assert L.sp24_values_bytes(10, 96, L.SP24_BF16, KB) == 2 * 10 * 64       # 96 = 1.5 blocks of 64
+    assert L.sp24_meta_bytes(10, 96, L.SP24_BF16, KB) == 2 * 10 * 8
+    assert L.sp24_values_bytes(10, 160, L.SP24_I8, KB) == 2 * 10 * 64        # 160 = 1.25 blocks of 128
+    assert L.sp24_meta_bytes(10, 160, L.SP24_I8, KB) == 2 * 10 * 16
+    assert L.sp24_values_bytes(4, 64, 99, ROW) == 0
+    assert L.sp24_values_bytes(4, 64, L.SP24_F16, 7) == 0
     assert L.sp24_gemm_workspace_bytes(8192, 8192, 8192, L.SP24_F16, L.SP24_F16) == 0
-    assert L.sp24_version() >= 100
+    assert L.sp24_version() >= 200
+
+
+def test_compressed_shapes_match_size_queries(L):
+    for dtype in (L.SP24_F16, L.SP24_I8):
+        for layout in (L.SP24_LAYOUT_ROW, L.SP24_LAYOUT_KBLOCK):
+            for M, K in [(1, 32), (7, 96), (300, 4096), (5, 160)]:
+                vs, ms = L.compressed_shapes(M, K, dtype, layout)
+                es = 2 if dtype == L.SP24_F16 else 1
+                assert int(np.prod(vs)) * es == L.sp24_values_bytes(M, K, dtype, layout)
+                assert int(np.prod(ms)) * 4 == L.sp24_meta_bytes(M, K, dtype, layout)
 
 
 def test_status_strings(L):
@@ -52,33 +72,44 @@ P = 1 << 20  # fake, 16-byte aligned device addresses: never touched on the erro
 
 def test_prune_compress_argument_errors(L):
     f = L.sp24_prune_compress
-    assert f(P, 2 * P, 3 * P, 4, 48, L.SP24_F16, None) == 1            # K % 32
-    assert f(P, 2 * P, 3 * P, -1, 64, L.SP24_F16, None) == 1           # negative M
-    assert f(P, 2 * P, 3 * P, 4, 64, 9, None) == 2                     # unknown dtype
-    assert f(P + 8, 2 * P, 3 * P, 4, 64, L.SP24_F16, None) == 3        # misaligned
-    assert f(P, P + 256, 3 * P, 4, 64, L.SP24_F16, None) == 1          # A overlaps A_vals
-    assert f(0, 2 * P, 3 * P, 4, 64, L.SP24_F16, None) == 1            # null
-    assert f(0, 0, 0, 0, 64, L.SP24_F16, None) == 0                    # empty: nothing enqueued
+    for lay in (L.SP24_LAYOUT_ROW, L.SP24_LAYOUT_KBLOCK):
+        assert f(P, 2 * P, 3 * P, 4, 48, L.SP24_F16, lay, None) == 1            # K % 32
+        assert f(P, 2 * P, 3 * P, -1, 64, L.SP24_F16, lay, None) == 1           # negative M
+        assert f(P, 2 * P, 3 * P, 4, 64, 9, lay, None) == 2                     # unknown dtype
+        assert f(P + 8, 2 * P, 3 * P, 4, 64, L.SP24_F16, lay, None) == 3        # misaligned
+        assert f(P, P + 256, 3 * P, 4, 64, L.SP24_F16, lay, None) == 1          # A overlaps A_vals
+        assert f(0, 2 * P, 3 * P, 4, 64, L.SP24_F16, lay, None) == 1            # null
+        assert f(0, 0, 0, 0, 64, L.SP24_F16, lay, None) == 0                    # empty: nothing enqueued
+    assert f(P, 2 * P, 3 * P, 4, 64, L.SP24_F16, 2, None) == 2                  # unknown layout
+    # K-blocked values of 4 rows x 96 columns take 2 blocks = 512 B: meta right after 256 B overlaps
+    assert f(P, 2 * P, 2 * P + 256, 4, 96, L.SP24_F16, L.SP24_LAYOUT_KBLOCK, None) == 1
 
 
 def test_gemm_argument_errors(L):
-    g = L.sp24_gemm
     F16, I8, E4, E5, BF = L.SP24_F16, L.SP24_I8, L.SP24_FP8_E4M3, L.SP24_BF8_E5M2, L.SP24_BF16
     A, Mt, B, C = P, 2 * P, 3 * P, 8 * P
-    assert g(A, Mt, F16, B, BF, C, 64, 64, 64, 1.0, 0.0, None, 0, None) == 2   # mixed 16-bit pair
-    assert g(A, Mt, F16, B, E4, C, 64, 64, 64, 1.0, 0.0, None, 0, None) == 2
-    assert g(A, Mt, I8, B, F16, C, 64, 64, 64, 1.0, 0.0, None, 0, None) == 2
-    assert g(A, Mt, F16, B, F16, C, 64, 64, 48, 1.0, 0.0, None, 0, None) == 1   # K % 32
-    assert g(A, Mt, F16, B, F16, C, 64, 12, 64, 1.0, 0.0, None, 0, None) == 2   # N*2 % 16
-    assert g(A, Mt, E4, B, E5, C, 64, 24, 64, 1.0, 0.0, None, 0, None) == 2     # N*1 % 16
-    assert g(A, Mt, I8, B, I8, C, 64, 64, 64, 2.0, 0.0, None, 0, None) == 2     # int8 alpha
-    assert g(A, Mt, I8, B, I8, C, 64, 64, 64, 1.0, 0.5, None, 0, None) == 2     # int8 beta
-    assert g(A, Mt, F16, B, F16, C + 4, 64, 64, 64, 1.0, 0.0, None, 0, None) == 3
-    assert g(A, Mt, F16, B, F16, B + 64, 64, 64, 64, 1.0, 0.0, None, 0, None) == 1  # C overlaps B
-    assert g(A, Mt, F16, B, F16, 0, 64, 64, 64, 1.0, 0.0, None, 0, None) == 1       # null C
-    assert g(A, Mt, F16, B, F16, C, 0, 64, 64, 1.0, 0.0, None, 0, None) == 0        # M == 0
-    assert g(A, Mt, F16, B, F16, C, 64, 0, 64, 1.0, 0.0, None, 0, None) == 0        # N == 0
-    assert g(A, Mt, F16, B, F16, C, -4, 64, 64, 1.0, 0.0, None, 0, None) == 1
-    # every documented pair passes validation up to the launch (checked with M == 0)
-    for a, b in [(F16, F16), (BF, BF), (I8, I8), (E4, E4), (E4, E5), (E5, E4), (E5, E5)]:
-        assert g(A, Mt, a, B, b, C, 0, 64, 64, 1.0, 0.0, None, 0, None) == 0
+    for lay in (L.SP24_LAYOUT_ROW, L.SP24_LAYOUT_KBLOCK):
+        def g(a, m, at, b, bt, c, *rest):
+            return L.sp24_gemm(a, m, at, lay, b, bt, c, *rest)
+        assert g(A, Mt, F16, B, BF, C, 64, 64, 64, 1.0, 0.0, None, 0, None) == 2   # mixed 16-bit pair
+        assert g(A, Mt, F16, B, E4, C, 64, 64, 64, 1.0, 0.0, None, 0, None) == 2
+        assert g(A, Mt, I8, B, F16, C, 64, 64, 64, 1.0, 0.0, None, 0, None) == 2
+        assert g(A, Mt, F16, B, F16, C, 64, 64, 48, 1.0, 0.0, None, 0, None) == 1   # K % 32
+        assert g(A, Mt, F16, B, F16, C, 64, 12, 64, 1.0, 0.0, None, 0, None) == 2   # N*2 % 16
+        assert g(A, Mt, E4, B, E5, C, 64, 24, 64, 1.0, 0.0, None, 0, None) == 2     # N*1 % 16
+        assert g(A, Mt, I8, B, I8, C, 64, 64, 64, 2.0, 0.0, None, 0, None) == 2     # int8 alpha
+        assert g(A, Mt, I8, B, I8, C, 64, 64, 64, 1.0, 0.5, None, 0, None) == 2     # int8 beta
+        assert g(A, Mt, F16, B, F16, C + 4, 64, 64, 64, 1.0, 0.0, None, 0, None) == 3
+        assert g(A, Mt, F16, B, F16, B + 64, 64, 64, 64, 1.0, 0.0, None, 0, None) == 1  # C overlaps B
+        assert g(A, Mt, F16, B, F16, 0, 64, 64, 64, 1.0, 0.0, None, 0, None) == 1       # null C
+        assert g(A, Mt, F16, B, F16, C, 0, 64, 64, 1.0, 0.0, None, 0, None) == 0        # M == 0
+        assert g(A, Mt, F16, B, F16, C, 64, 0, 64, 1.0, 0.0, None, 0, None) == 0        # N == 0
+        assert g(A, Mt, F16, B, F16, C, -4, 64, 64, 1.0, 0.0, None, 0, None) == 1
+        assert g(A, Mt, F16, B, F16, C, 64, 1 << 23, 64, 1.0, 0.0, None, 0, None) == 2  # 128 rows of B > 2 GiB
+        # every documented pair passes validation up to the launch (checked with M == 0)
+        for a, b in [(F16, F16), (BF, BF), (I8, I8), (E4, E4), (E4, E5), (E5, E4), (E5, E5)]:
+            assert g(A, Mt, a, B, b, C, 0, 64, 64, 1.0, 0.0, None, 0, None) == 0
+    assert L.sp24_gemm(A, Mt, F16, 5, B, F16, C, 64, 64, 64, 1.0, 0.0, None, 0, None) == 2   # unknown layout
+    # the row-major layout addresses a 256-row tile with 32-bit offsets: K is bounded
+    big_k = 1 << 23
+    assert L.sp24_gemm(A, Mt, F16, L.SP24_LAYOUT_ROW, B, F16, C, 64, 64, big_k, 1.0, 0.0, None, 0, None) == 2
