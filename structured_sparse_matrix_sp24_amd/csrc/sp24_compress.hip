@@ -121,10 +121,11 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kernel(const 
 
 // K-blocked layout.  Workgroup (row tile rt, block b) covers rows
 // rt*128 .. +128 of block b; thread t handles chunk t%8 of rows
-// rt*128 + t/8 + 32u (u < 4).  Consecutive workgroups take consecutive row
-// tiles of the same block, so the outputs of neighbouring workgroups are
-// neighbours in memory.  Chunks past K (the tail of a partial last block)
-// are written as zero values with zero codes.
+// rt*128 + t/8 + 32u (u < 4).  Consecutive workgroups take consecutive
+// blocks of the same row tile, so the workgroups in flight read one
+// contiguous band of A (DRAM-page friendly) while each writes one 8 KiB run
+// of values.  Chunks past K (the tail of a partial last block) are written
+// as zero values with zero codes.
 constexpr int kKbRowsPerTile = 128;
 
 template <int ES, bool INT>
@@ -132,11 +133,11 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kblock_kernel
                                                                                    char* __restrict__ vals,
                                                                                    char* __restrict__ meta,
                                                                                    int64_t M, int64_t K,
-                                                                                   uint32_t row_tiles) {
+                                                                                   uint32_t nblk) {
   constexpr int MB = ES == 2 ? 8 : 16;         // metadata bytes per row per block
   constexpr int CE = 16 / ES;                   // dense elements per chunk
-  const uint32_t rt = blockIdx.x % row_tiles;
-  const int64_t b = blockIdx.x / row_tiles;
+  const int64_t b = blockIdx.x % nblk;
+  const uint32_t rt = blockIdx.x / nblk;
   const int c = threadIdx.x & 7;
   const int64_t kcol = b * (8 * CE) + (int64_t)c * CE;  // first dense column of the chunk
   const bool inside = kcol < K;
@@ -200,10 +201,10 @@ hipError_t launch_prune_compress(const void* A, void* vals, uint32_t* meta, int6
     const char* a = static_cast<const char*>(A);
     char* v = static_cast<char*>(vals);
     char* m = reinterpret_cast<char*>(meta);
-    const uint32_t rt = (uint32_t)row_tiles;
-    if (es == 2) hipLaunchKernelGGL((prune_compress_kblock_kernel<2, false>), grid, block, 0, stream, a, v, m, M, K, rt);
-    else if (is_int) hipLaunchKernelGGL((prune_compress_kblock_kernel<1, true>), grid, block, 0, stream, a, v, m, M, K, rt);
-    else hipLaunchKernelGGL((prune_compress_kblock_kernel<1, false>), grid, block, 0, stream, a, v, m, M, K, rt);
+    const uint32_t nb = (uint32_t)nblk;
+    if (es == 2) hipLaunchKernelGGL((prune_compress_kblock_kernel<2, false>), grid, block, 0, stream, a, v, m, M, K, nb);
+    else if (is_int) hipLaunchKernelGGL((prune_compress_kblock_kernel<1, true>), grid, block, 0, stream, a, v, m, M, K, nb);
+    else hipLaunchKernelGGL((prune_compress_kblock_kernel<1, false>), grid, block, 0, stream, a, v, m, M, K, nb);
     return hipGetLastError();
   }
   const int64_t nchunks = M * K * es / 16;
