@@ -118,10 +118,22 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--gemm-only-launches", type=int, default=0,
                     help="after the timed steps, launch only the GEMM this many times (for profilers)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes 5 times (counter calibration) and exit")
     args = ap.parse_args()
 
+    if args.copy_bytes:
+        import torch
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": 5}), flush=True)
+        return
+
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the 2:4 path has no inter-GPU step); "
+        print("bench.py runs on one GPU only (the 2:4 path has no inter-GPU step); "
               "--gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
