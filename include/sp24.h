@@ -101,10 +101,11 @@ size_t sp24_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int a_type, in
  * sp24_prune_compress -- dense A -> (A_vals, meta).
  *
  * Prunes every group of 4 consecutive K-elements of each row to its two
- * largest-magnitude elements and compresses the result (pages: "walk the K
- * dimension in groups of four, extract the two non-zero positions, and pack
- * them consecutively"; which two to keep is not fixed by the pages, which
- * leave pruning to an offline pass).  Magnitude is compared on the bit
+ * largest-magnitude elements and compresses the result: the two kept values
+ * of each group are stored one after the other and their positions become
+ * the group's codes ("CDNA and CDNA2 sparse MFMA builtins", section
+ * "Structured sparsity (4:2 pattern)").  Which two to keep is not fixed by
+ * the pages, which leave pruning to an offline pass.  Magnitude is compared on the bit
  * pattern with the sign cleared (float types; NaN ranks above Inf, -0 equals
  * +0) or |x| (int8, -128 ranks highest); on equal magnitude the lower
  * position wins.  Kept values are copied bit for bit.  An A that is already
@@ -126,10 +127,12 @@ int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, 
  * sp24_gemm -- D = alpha * expand(A_vals, meta) * B + beta * C, D written
  * over C.
  *
- * The hardware form is the sparse matrix-core instruction (pages: the index
- * "aligns the compressed A elements against the correct rows of B"; the ISA
- * page: "D = A (sparse) * B + D").  Products of the supported inputs are
- * exact in fp32; sums are fp32 (exact int32 for int8).
+ * The hardware form is the sparse matrix-core instruction: each compressed A
+ * value is multiplied with the row of B its position code selects, and the
+ * products accumulate into D ("CDNA and CDNA2 sparse MFMA builtins", section
+ * "Structured sparsity (4:2 pattern)"; the ISA page for
+ * v_smfmac_f32_32x32x32_bf8_bf8, section "Semantics").  Products of the
+ * supported inputs are exact in fp32; sums are fp32 (exact int32 for int8).
  *
  *   A_vals, meta  compressed A in `layout`, as produced by
  *                 sp24_prune_compress (or any caller-built data in the same
