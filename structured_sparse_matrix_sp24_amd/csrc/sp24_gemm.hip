@@ -51,25 +51,25 @@ __host__ __device__ constexpr int meta_step_bytes() { return op_esize(OP) == 2 ?
 //
 // Ping-pong schedule.  The two wave groups (waves 0-3 and 4-7) run half a
 // k-step apart, in phases separated by workgroup barriers.  In every phase
-// one group issues the 32 MFMAs of its current step back to back while the
-// other group stages data: it reads its next fragments from LDS and issues
-// its share of a later step's global -> LDS loads.  Each SIMD thus always
-// has one wave feeding the matrix core, and the waves that block on load
-// issue (the vector-memory path needs about as long per k-step as the matrix
-// core) are never the ones the matrix core is waiting for.
+// one group issues the 32 MFMAs of its current step, with its share of a
+// later step's global -> LDS loads slotted in after every four MFMAs, while
+// the other group reads its next fragments from LDS.  Each SIMD thus always
+// has one wave feeding the matrix core, and the LDS reads never queue behind
+// a load instruction waiting for the vector-memory path.
 //
-//   phase 2k    group 0: MFMAs of step k      group 1: reads step k,
-//                                                        loads step k+2
-//   phase 2k+1  group 0: reads step k+1,      group 1: MFMAs of step k
-//                        loads step k+3
+//   phase 2k    group 0: MFMAs of step k,     group 1: reads step k
+//                        loads step k+2
+//   phase 2k+1  group 0: reads step k+1       group 1: MFMAs of step k,
+//                                                      loads step k+3
 //
 // Staging: three LDS stages of one k-step each (A values 16 KiB | B 32 KiB |
 // metadata 2 or 4 KiB), filled by buffer loads that write LDS directly,
 // issued through inline assembly and waited for with explicit vmcnt counts.
-// Every wave loads a fixed share of every step (7 or 8 instructions).  At
-// the end of phase 2k each wave waits for its share of step k+1, so the
-// barrier publishes that step before group 0 reads it; a stage is rewritten
-// (step j+3 into the stage of step j) only after both groups have read it.
+// Every wave loads a fixed share of every step (7 or 8 instructions); group 1
+// loads step j in phase 2j-5 and group 0 in phase 2j-4, after both groups
+// have read step j-3 from the same stage (phases 2j-7 and 2j-6).  At the end
+// of phase 2k each wave waits for its share of step k+1, so the barrier
+// publishes that step before group 0 reads it in phase 2k+1.
 // ----------------------------------------------------------------------------
 constexpr int kBM = 256, kBN = 256, kThreads8 = 512;
 constexpr int kLdsA = kBM * 64;                   // 16 KiB
@@ -174,55 +174,74 @@ struct TileArgs {
   int M, N, m0, n0, nsteps, nfull;
 };
 
-// Load instruction P of this wave's share of k-step j into stage `st`:
+// Buffer resources and LDS base of this wave's loads for k-step j (scalar
+// work only, computed ahead of the phase that issues the loads).  Loads are
+// issued for every j, also past the last step: those get empty buffer ranges
+// and read nothing, which keeps the per-step load count uniform.  B rows
+// past K and rows past M read as zero through the buffer range check.
+struct DmaStep {
+  i32x4 rA, rB, rM;
+  uint32_t lds;      // LDS byte address of the stage
+  uint32_t offA;     // ROW layout: byte offset of the step inside a row of A
+  uint32_t offM;     // ROW layout: same for the metadata
+  bool tail;         // the step ends past K (masking needed)
+  int64_t validA;    // bytes of the step inside a row of A
+  int64_t validM;    // ROW layout: bytes of the step inside a metadata row
+};
+
+template <int OP, int LAYOUT>
+__device__ __forceinline__ DmaStep make_dma_step(SP24_LDS char* st, const TileArgs& ta, int j) {
+  constexpr int KS = op_kstep(OP), ES = op_esize(OP), MB = meta_step_bytes<OP>();
+  DmaStep d;
+  d.lds = lds_addr(st);
+  d.tail = j >= ta.nfull;
+  d.validA = ta.rowA - (int64_t)j * 64;
+  d.validM = ta.rowM - (int64_t)j * MB;
+  if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK) {
+    const bool in = j < ta.nsteps;
+    d.rA = make_rsrc4(ta.A_vals + ((int64_t)j * ta.M + ta.m0) * 64, in ? (uint64_t)(ta.M - ta.m0) * 64 : 0u);
+    d.rM = make_rsrc4(ta.meta + ((int64_t)j * ta.M + ta.m0) * MB, in ? (uint64_t)(ta.M - ta.m0) * MB : 0u);
+    d.offA = d.offM = 0;
+  } else {
+    d.rA = ta.rA;
+    d.rM = ta.rM;
+    d.offA = (uint32_t)(j * 64);
+    d.offM = (uint32_t)(j * MB);
+  }
+  const int64_t start = ((int64_t)j * KS * ta.N + ta.n0) * ES;
+  d.rB = make_rsrc4(ta.B + start, start < ta.btotal ? (uint64_t)(ta.btotal - start) : 0u);
+  return d;
+}
+
+// Load instruction P of this wave's share of a k-step (resources in `d`):
 //   P = 0, 1   A values, tile rows 16*(2w+P) .. +16 (64 B each);
 //   P = 2..5   B, 1 KiB block 4w+P-2 of the step;
 //   P = 6, 7   metadata piece P-6 (8-bit inputs load two, 16-bit one).
-// Loads are issued for every j, also past the last step: those read nothing
-// (empty buffer range) and keep the per-step count uniform.  In a step that
-// ends past K (the last one when K is not a multiple of KS, and those past
-// the end) the lanes past the row end are masked; B rows past K and rows
-// past M read as zero through the buffer range check.
+// In a step that ends past K (the last one when K is not a multiple of KS,
+// and those past the end) lanes past the row end are masked.
 template <int OP, int LAYOUT, int P>
-__device__ __forceinline__ void dma_piece(SP24_LDS char* st, const LaneConsts8& lc, const TileArgs& ta, int w,
-                                          int j) {
-  constexpr int KS = op_kstep(OP), ES = op_esize(OP), MB = meta_step_bytes<OP>();
-  constexpr bool KB = LAYOUT == SP24_LAYOUT_KBLOCK;
-  const bool tail = j >= ta.nfull;  // wave-uniform
+__device__ __forceinline__ void dma_piece(const DmaStep& d, const LaneConsts8& lc, int w) {
+  constexpr int ES = op_esize(OP);
   if constexpr (P < 2) {
-    i32x4 r;
-    uint32_t off = lc.voA[P];
-    if constexpr (KB) {
-      r = make_rsrc4(ta.A_vals + ((int64_t)j * ta.M + ta.m0) * 64, j < ta.nsteps ? (uint64_t)(ta.M - ta.m0) * 64 : 0u);
-    } else {
-      r = ta.rA;
-      off += (uint32_t)(j * 64);
-    }
-    if (tail) {
+    uint32_t off = lc.voA[P] + d.offA;
+    if (d.tail) {
       const int l = lane_id();
       const int row = (w * 2 + P) * 16 + (l >> 2);
-      if (16 * ((l & 3) ^ swzA(row)) >= ta.rowA - (int64_t)j * 64) off = kOOB;
+      if (16 * ((l & 3) ^ swzA(row)) >= d.validA) off = kOOB;
     }
-    dma16_asm(r, lds_addr(st) + (w * 2 + P) * 1024, off, 0u);
+    dma16_asm(d.rA, d.lds + (w * 2 + P) * 1024, off, 0u);
   } else if constexpr (P < 6) {
-    const int64_t start = ((int64_t)j * KS * ta.N + ta.n0) * ES;
-    const i32x4 rB = make_rsrc4(ta.B + start, start < ta.btotal ? (uint64_t)(ta.btotal - start) : 0u);
-    dma16_asm(rB, lds_addr(st) + kLdsA + (w * 4 + P - 2) * 1024, lc.voB[P - 2], 0u);
+    dma16_asm(d.rB, d.lds + kLdsA + (w * 4 + P - 2) * 1024, lc.voB[P - 2], 0u);
   } else {
     constexpr int i = P - 6;
-    i32x4 r;
-    uint32_t off = lc.voM[i];
-    if constexpr (KB) {
-      r = make_rsrc4(ta.meta + ((int64_t)j * ta.M + ta.m0) * MB, j < ta.nsteps ? (uint64_t)(ta.M - ta.m0) * MB : 0u);
-    } else {
-      r = ta.rM;
-      off += (uint32_t)(j * MB);
-      if (tail) {
+    uint32_t off = lc.voM[i] + d.offM;
+    if constexpr (LAYOUT == SP24_LAYOUT_ROW) {
+      if (d.tail) {
         const int l = lane_id();
-        if ((int64_t)j * MB + (ES == 2 ? 4 * (l & 1) : 4 * (l & 3)) >= ta.rowM) off = kOOB;
+        if ((ES == 2 ? 4 * (l & 1) : 4 * (l & 3)) >= d.validM) off = kOOB;
       }
     }
-    dma4_asm(r, lds_addr(st) + kLdsA + kLdsB + (ES == 2 ? w * 256 : w * 512 + i * 256), off, 0u);
+    dma4_asm(d.rM, d.lds + kLdsA + kLdsB + (ES == 2 ? w * 256 : w * 512 + i * 256), off, 0u);
   }
 }
 
@@ -333,68 +352,71 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   };
   // All loads of this wave's share of step j, back to back (pipeline fill).
   auto dma_all = [&](int j) {
-    SP24_LDS char* dst = st(j % 3);
-    dma_piece<OP, LAYOUT, 0>(dst, lc, ta, w, j);
-    dma_piece<OP, LAYOUT, 1>(dst, lc, ta, w, j);
-    dma_piece<OP, LAYOUT, 2>(dst, lc, ta, w, j);
-    dma_piece<OP, LAYOUT, 3>(dst, lc, ta, w, j);
-    dma_piece<OP, LAYOUT, 4>(dst, lc, ta, w, j);
-    dma_piece<OP, LAYOUT, 5>(dst, lc, ta, w, j);
-    dma_piece<OP, LAYOUT, 6>(dst, lc, ta, w, j);
-    if constexpr (L == 8) dma_piece<OP, LAYOUT, 7>(dst, lc, ta, w, j);
+    const DmaStep d = make_dma_step<OP, LAYOUT>(st(j % 3), ta, j);
+    dma_piece<OP, LAYOUT, 0>(d, lc, w);
+    dma_piece<OP, LAYOUT, 1>(d, lc, w);
+    dma_piece<OP, LAYOUT, 2>(d, lc, w);
+    dma_piece<OP, LAYOUT, 3>(d, lc, w);
+    dma_piece<OP, LAYOUT, 4>(d, lc, w);
+    dma_piece<OP, LAYOUT, 5>(d, lc, w);
+    dma_piece<OP, LAYOUT, 6>(d, lc, w);
+    if constexpr (L == 8) dma_piece<OP, LAYOUT, 7>(d, lc, w);
   };
-  // Staging phase: the fragments of step jr, each group of four reads
-  // followed by one load instruction of step jd.
-  auto stage_phase = [&](int jr, int jd) {
+  // Staging phase: the fragments of step jr.
+  auto stage_phase = [&](int jr) {
     const SP24_LDS char* cur = st(jr % 3);
-    SP24_LDS char* dst = st(jd % 3);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      read_group(cur, g);
-      if (g == 0) dma_piece<OP, LAYOUT, 0>(dst, lc, ta, w, jd);
-      if (g == 1) dma_piece<OP, LAYOUT, 1>(dst, lc, ta, w, jd);
-      if (g == 2) dma_piece<OP, LAYOUT, 2>(dst, lc, ta, w, jd);
-      if (g == 3) dma_piece<OP, LAYOUT, 3>(dst, lc, ta, w, jd);
-      if (g == 4) dma_piece<OP, LAYOUT, 4>(dst, lc, ta, w, jd);
-      if (g == 5) dma_piece<OP, LAYOUT, 5>(dst, lc, ta, w, jd);
-      if (g == 6) dma_piece<OP, LAYOUT, 6>(dst, lc, ta, w, jd);
+    for (int g = 0; g < 8; ++g) read_group(cur, g);
+  };
+  // Matrix phase: the 32 MFMAs of the fragments in registers, one load
+  // instruction of the step described by `d` after each group of four.
+  auto mfma_phase = [&](const DmaStep& d) {
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm) {
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = smfmac16<OP>(acc[tm][tn], f.a[tm], f.b[tn], f.idx[tm]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (tm == 0) dma_piece<OP, LAYOUT, 0>(d, lc, w);
+      if (tm == 1) dma_piece<OP, LAYOUT, 2>(d, lc, w);
+      if (tm == 2) dma_piece<OP, LAYOUT, 3>(d, lc, w);
+      if (tm == 3) dma_piece<OP, LAYOUT, 1>(d, lc, w);
+      if (tm == 4) dma_piece<OP, LAYOUT, 4>(d, lc, w);
+      if (tm == 5) dma_piece<OP, LAYOUT, 5>(d, lc, w);
+      if (tm == 6) dma_piece<OP, LAYOUT, 6>(d, lc, w);
       if constexpr (L == 8)
-        if (g == 7) dma_piece<OP, LAYOUT, 7>(dst, lc, ta, w, jd);
+        if (tm == 7) dma_piece<OP, LAYOUT, 7>(d, lc, w);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Matrix phase: the 32 MFMAs of the fragments in registers.
-  auto mfma_phase = [&]() {
-#pragma unroll
-    for (int tm = 0; tm < 8; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = smfmac16<OP>(acc[tm][tn], f.a[tm], f.b[tn], f.idx[tm]);
-  };
 
-  // Fill: steps 0 and 1 (and group 0's share of step 2, which it would have
+  // Fill: steps 0 and 1 (and group 1's share of step 2, which it would have
   // loaded in the phase before phase 0); group 0 reads step 0.  Loads past
   // the last step read nothing.  The two groups run separate loops with the
   // same sequence of barriers.
   dma_all(0);
   dma_all(1);
+  // The buffer resources of the loads a matrix phase issues are computed
+  // during the staging phase before it, so the matrix phase only sets the LDS
+  // address and issues each load between its MFMAs.
   if (g0) {
-    dma_all(2);
-    phase_end<2 * L>();  // this wave's share of step 0 has landed
-    const SP24_LDS char* cur = st(0);
-#pragma unroll
-    for (int g = 0; g < 8; ++g) read_group(cur, g);
+    phase_end<L>();  // this wave's share of step 0 has landed
+    stage_phase(0);
+    DmaStep d = make_dma_step<OP, LAYOUT>(st(2), ta, 2);
     for (int k = 0; k < nsteps; ++k) {
-      mfma_phase();               // phase 2k: step k
+      mfma_phase(d);              // phase 2k: step k, loads of step k+2
       phase_end<L>();             // this wave's share of step k+1 has landed
-      stage_phase(k + 1, k + 3);  // phase 2k+1
+      stage_phase(k + 1);         // phase 2k+1
+      d = make_dma_step<OP, LAYOUT>(st((k + 3) % 3), ta, k + 3);
       phase_end<63>();            // the reads of step k+1 are done
     }
   } else {
-    phase_end<L>();
+    dma_all(2);
+    phase_end<2 * L>();
     for (int k = 0; k < nsteps; ++k) {
-      stage_phase(k, k + 2);      // phase 2k
+      stage_phase(k);             // phase 2k
+      const DmaStep d = make_dma_step<OP, LAYOUT>(st(k % 3), ta, k + 3);
       phase_end<L>();             // this wave's share of step k+1 has landed, the reads of step k are done
-      mfma_phase();               // phase 2k+1: step k
+      mfma_phase(d);              // phase 2k+1: step k, loads of step k+3
       phase_end<63>();
     }
   }
