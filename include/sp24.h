@@ -29,11 +29,22 @@
  *   SP24_LAYOUT_KBLOCK  GEMM-ready: K is cut into blocks of KB dense columns
  *                       (KB = 64 for 16-bit types, 128 for 8-bit types; each
  *                       block is 64 bytes of compressed values per row), and
- *                       block b of all M rows is stored together:
- *                         A_vals bytes [(b*M + i)*64, +64) = row i, block b;
- *                         meta words   [(b*M + i)*W, +W)   = row i, block b,
- *                       with W = KB/32 words (2 or 4).  ceil(K/KB) blocks;
- *                       the tail of a last partial block is zero.  One
+ *                       block b of all rows is stored together.  ceil(K/KB)
+ *                       blocks; the tail of a last partial block is zero.
+ *                       Values: bytes [(b*M + i)*64, +64) = row i, block b.
+ *                       Metadata: per block, Mp = M rounded up to 128 rows,
+ *                       MB = KB/8 bytes per row (8 or 16), block b at bytes
+ *                       [b*Mp*MB, +Mp*MB), rows past M zero.  A row's codes
+ *                       for the block are 4 words c_0..c_3 (16 bits each for
+ *                       16-bit types, 32 bits for 8-bit types; word g holds
+ *                       the codes of the row's compressed elements
+ *                       KB/8*g .. in the order above).  Inside block b, the
+ *                       words of the 128 rows 128p+16t+r (t < 8, r < 16) are
+ *                       stored, from byte (b*Mp + 128p)*MB on,
+ *                         16-bit: u16 index ((r*4 + g)*4 + t/2)*2 + t%2,
+ *                         8-bit:  u32 index  (r*4 + g)*8 + t,
+ *                       so the 8 words one matrix-core lane needs for the 8
+ *                       row tiles of a 128-row group are contiguous.  One
  *                       k-step of a 256-row tile is then a single contiguous
  *                       16 KiB run of values and 2 or 4 KiB of metadata.
  *
@@ -90,7 +101,8 @@ typedef enum {
  * Returns 0 for an unknown dtype or layout or negative sizes. */
 size_t sp24_values_bytes(int64_t M, int64_t K, int dtype, int layout);
 
-/* Bytes of the metadata: ROW: M * (K/32) * 4; KBLOCK: ceil(K/KB) * M * KB/8. */
+/* Bytes of the metadata: ROW: M * (K/32) * 4; KBLOCK: ceil(K/KB) * Mp * KB/8
+ * with Mp = M rounded up to a multiple of 128. */
 size_t sp24_meta_bytes(int64_t M, int64_t K, int dtype, int layout);
 
 /* Workspace that sp24_gemm needs for this problem (currently always 0: the

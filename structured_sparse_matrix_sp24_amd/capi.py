@@ -123,7 +123,8 @@ def compressed_shapes(M: int, K: int, dtype: int, layout: int):
     if layout == SP24_LAYOUT_KBLOCK:
         kb = kblock_width(dtype)
         nblk = -(-K // kb)
-        return (nblk, M, kb // 2), (nblk, M, kb // 32)
+        mp = -(-M // 128) * 128  # metadata rows are padded to whole 128-row groups
+        return (nblk, M, kb // 2), (nblk, mp, kb // 32)
     raise ValueError(f"unknown layout {layout}")
 
 
@@ -131,8 +132,9 @@ def prune_compress(A, dtype: int | None = None, layout: int = SP24_LAYOUT_KBLOCK
     """A: M x K device tensor (any 1- or 2-byte dtype holding the bits of
     ``dtype``).  Returns (A_vals, meta) in ``layout``: ROW gives M x K/2 values
     and M x K/32 metadata words; KBLOCK gives nblk x M x KB/2 values and
-    nblk x M x KB/32 words (KB = kblock_width(dtype)).  Metadata words are
-    uint32 held in int32 tensors."""
+    nblk x Mp x KB/32 words (KB = kblock_width(dtype), Mp = M rounded up to
+    128, words interleaved in 128-row groups as include/sp24.h describes).
+    Metadata words are uint32 held in int32 tensors."""
     import torch
     if dtype is None:
         dtype = dtype_code(A.dtype)

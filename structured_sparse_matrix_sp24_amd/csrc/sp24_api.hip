@@ -68,7 +68,7 @@ size_t sp24_values_bytes(int64_t M, int64_t K, int dtype, int layout) {
 size_t sp24_meta_bytes(int64_t M, int64_t K, int dtype, int layout) {
   const int es = esize(dtype);
   if (es == 0 || M < 0 || K < 0 || !layout_ok(layout)) return 0;
-  if (layout == SP24_LAYOUT_KBLOCK) return (size_t)kblocks(K, es) * (size_t)M * (es == 2 ? 8u : 16u);
+  if (layout == SP24_LAYOUT_KBLOCK) return (size_t)kblocks(K, es) * (size_t)((M + 127) / 128 * 128) * (es == 2 ? 8u : 16u);
   return (size_t)M * (size_t)(K / 32) * 4u;
 }
 

@@ -125,7 +125,14 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kernel(const 
 // blocks of the same row tile, so the workgroups in flight read one
 // contiguous band of A (DRAM-page friendly) while each writes one 8 KiB run
 // of values.  Chunks past K (the tail of a partial last block) are written
-// as zero values with zero codes.
+// as zero values with zero codes, and rows past M up to the 128-row group
+// boundary get zero codes (the metadata is padded to whole groups).
+//
+// A chunk's codes are half of a code word: chunk c of a row
+// holds half c%2 of the row's word g = c/2 (bytes for 16-bit types, 16-bit
+// halves for 8-bit types).  In the 128-row group, word g of row 16t + r sits
+// at u16 index ((r*4 + g)*4 + t/2)*2 + t%2 (16-bit types) or u32 index
+// (r*4 + g)*8 + t (8-bit types).
 constexpr int kKbRowsPerTile = 128;
 
 template <int ES, bool INT>
@@ -138,6 +145,7 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kblock_kernel
   constexpr int CE = 16 / ES;                   // dense elements per chunk
   const int64_t b = blockIdx.x % nblk;
   const uint32_t rt = blockIdx.x / nblk;
+  const int64_t Mp = (M + 127) / 128 * 128;
   const int c = threadIdx.x & 7;
   const int64_t kcol = b * (8 * CE) + (int64_t)c * CE;  // first dense column of the chunk
   const bool inside = kcol < K;
@@ -152,8 +160,17 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kblock_kernel
   }
 #pragma unroll
   for (int u = 0; u < kCompressUnroll; ++u) {
-    const int64_t row = (int64_t)rt * kKbRowsPerTile + (threadIdx.x >> 3) + 32 * u;
-    if (row >= M) break;
+    const int rr = (threadIdx.x >> 3) + 32 * u;  // row inside the 128-row group
+    const int64_t row = (int64_t)rt * kKbRowsPerTile + rr;
+    const int t = rr >> 4, r = rr & 15;
+    char* mgroup = meta + (b * Mp + (int64_t)rt * 128) * MB;
+    if (row >= M) {  // padding rows of the last group: zero codes
+      if constexpr (ES == 2)
+        __builtin_nontemporal_store((uint8_t)0, reinterpret_cast<uint8_t*>(mgroup + (((r * 4 + c / 2) * 4 + t / 2) * 2 + (t & 1)) * 2 + (c & 1)));
+      else
+        __builtin_nontemporal_store((uint16_t)0, reinterpret_cast<uint16_t*>(mgroup + ((r * 4 + c / 2) * 8 + t) * 4 + (c & 1) * 2));
+      continue;
+    }
     const int64_t slot = b * M + row;
     const uint32_t d0 = (uint32_t)in[u][0], d1 = (uint32_t)in[u][1];
     const uint32_t d2 = (uint32_t)in[u][2], d3 = (uint32_t)in[u][3];
@@ -168,7 +185,7 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kblock_kernel
         code = (uint8_t)(n0 | (n1 << 4));
       }
       __builtin_nontemporal_store(out, vp);
-      __builtin_nontemporal_store(code, reinterpret_cast<uint8_t*>(meta + slot * MB + c));
+      __builtin_nontemporal_store(code, reinterpret_cast<uint8_t*>(mgroup + (((r * 4 + c / 2) * 4 + t / 2) * 2 + (t & 1)) * 2 + (c & 1)));
     } else {
       uint16_t code = 0;
       if (inside) {
@@ -180,7 +197,7 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kblock_kernel
         code = (uint16_t)(n0 | (n1 << 4) | (n2 << 8) | (n3 << 12));
       }
       __builtin_nontemporal_store(out, vp);
-      __builtin_nontemporal_store(code, reinterpret_cast<uint16_t*>(meta + slot * MB + 2 * c));
+      __builtin_nontemporal_store(code, reinterpret_cast<uint16_t*>(mgroup + ((r * 4 + c / 2) * 8 + t) * 4 + (c & 1) * 2));
     }
   }
 }

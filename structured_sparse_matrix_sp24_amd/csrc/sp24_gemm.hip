@@ -34,11 +34,15 @@ namespace sp24 {
 // ----------------------------------------------------------------------------
 // Compressed layouts (sp24_layout).  ROW: A_vals M x K/2 elements and meta
 // M x K/32 words, both row-major.  KBLOCK: K is cut into blocks of one k-step
-// (KS dense columns, 64 bytes of values per row), and block b of all M rows
-// is stored together: values of row i at (b*M + i)*64, metadata at
-// (b*M + i)*MB with MB = 8 (16-bit) or 16 (8-bit) bytes.  In KBLOCK one
-// k-step of a row tile is a single contiguous run of values and one of
-// metadata; in ROW it is one short piece per row.
+// (KS dense columns, 64 bytes of values per row), and block b of all rows is
+// stored together: values of row i at (b*M + i)*64; metadata MB = 8 (16-bit)
+// or 16 (8-bit) bytes per row, rows padded to Mp (a multiple of 128), with
+// the 4 code words of the rows of each 128-row group interleaved so that the
+// 8 words one lane needs for the group's 8 row tiles are contiguous (16-bit
+// types: word g of row 16t+r at u16 index ((r*4+g)*4 + t/2)*2 + t%2; 8-bit
+// types: at u32 index (r*4+g)*8 + t).  In KBLOCK one k-step of a row tile is
+// a single contiguous run of values and one of metadata; in ROW it is one
+// short piece per row.
 // ----------------------------------------------------------------------------
 template <int OP>
 __host__ __device__ constexpr int meta_step_bytes() { return op_esize(OP) == 2 ? 8 : 16; }
@@ -97,7 +101,7 @@ struct LaneConsts8 {
   uint32_t voB[4];  // B: 1 KiB blocks 4w+i of the step
   uint32_t voM[2];  // metadata: rows 32w .. +32 of the tile
   int ldsA;         // A fragment read offset
-  int ldsM;         // idx read offset (inside the stage's metadata)
+  int ldsM;         // idx read offset (inside the stage)
   int ldsB[4];      // B transpose-read base of each column tile
 };
 
@@ -137,7 +141,10 @@ __device__ __forceinline__ LaneConsts8 make_lane_consts8(int w, int l, int64_t r
   }
   const int wm = w >> 2, wn = w & 3, ga = l >> 4, r16 = l & 15;
   c.ldsA = (wm * 128 + r16) * 64 + 16 * (ga ^ swzA(r16));
-  c.ldsM = kLdsA + kLdsB + (wm * 128 + r16) * MB + (ES == 2 ? 2 * ga : 4 * ga);
+  if constexpr (KB)  // this lane's 8 words of its 128-row group, contiguous
+    c.ldsM = kLdsA + kLdsB + wm * 128 * MB + (r16 * 4 + ga) * (ES == 2 ? 16 : 32);
+  else               // [row][MB]
+    c.ldsM = kLdsA + kLdsB + (wm * 128 + r16) * MB + (ES == 2 ? 2 * ga : 4 * ga);
   const int gb = l >> 4, s = l & 15;
 #pragma unroll
   for (int tn = 0; tn < 4; ++tn) {
@@ -153,11 +160,14 @@ __device__ __forceinline__ LaneConsts8 make_lane_consts8(int w, int l, int64_t r
   return c;
 }
 
-// Fragments of one k-step for one wave: 8 A rows of 16, their idx words, and
-// 4 B column tiles.
+// Fragments of one k-step for one wave: 8 A rows of 16, their idx words
+// (ROW: one register per row tile; KBLOCK: the 8 words in one or two vector
+// reads, two 16-bit words per register for 16-bit types), and 4 B column
+// tiles.
 struct Frags8 {
   i32x4 a[8];
   int idx[8];
+  i32x4 idxv[2];
   i32x8 b[4];
 };
 
@@ -172,6 +182,7 @@ struct TileArgs {
   int64_t rowM;    // metadata bytes per row (ROW stride; both: K tail)
   int64_t btotal;  // bytes of B
   int M, N, m0, n0, nsteps, nfull;
+  int Mp;          // KBLOCK: metadata rows per block (M rounded up to 128)
 };
 
 // Buffer resources and LDS base of this wave's loads for k-step j (scalar
@@ -200,7 +211,7 @@ __device__ __forceinline__ DmaStep make_dma_step(SP24_LDS char* st, const TileAr
   if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK) {
     const bool in = j < ta.nsteps;
     d.rA = make_rsrc4(ta.A_vals + ((int64_t)j * ta.M + ta.m0) * 64, in ? (uint64_t)(ta.M - ta.m0) * 64 : 0u);
-    d.rM = make_rsrc4(ta.meta + ((int64_t)j * ta.M + ta.m0) * MB, in ? (uint64_t)(ta.M - ta.m0) * MB : 0u);
+    d.rM = make_rsrc4(ta.meta + ((int64_t)j * ta.Mp + ta.m0) * MB, in ? (uint64_t)(ta.Mp - ta.m0) * MB : 0u);
     d.offA = d.offM = 0;
   } else {
     d.rA = ta.rA;
@@ -306,6 +317,7 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   ta.n0 = n0;
   ta.nsteps = (K + KS - 1) / KS;
   ta.nfull = K / KS;
+  ta.Mp = (M + 127) / 128 * 128;
   if constexpr (LAYOUT == SP24_LAYOUT_ROW) {
     ta.rA = make_rsrc4(A_vals + (int64_t)m0 * ta.rowA, (int64_t)(M - m0) * ta.rowA);
     ta.rM = make_rsrc4(meta + (int64_t)m0 * ta.rowM, (int64_t)(M - m0) * ta.rowM);
@@ -345,8 +357,15 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
       for (int h = 0; h < 2; ++h) {
         const int tm = 2 * (grp - 4) + h;
         f.a[tm] = *(const SP24_LDS i32x4*)(cur + lc.ldsA + tm * 1024);
-        if constexpr (ES == 2) f.idx[tm] = *(const SP24_LDS unsigned short*)(cur + lc.ldsM + tm * 16 * MB);
-        else f.idx[tm] = *(const SP24_LDS int*)(cur + lc.ldsM + tm * 16 * MB);
+        if constexpr (LAYOUT == SP24_LAYOUT_ROW) {
+          if constexpr (ES == 2) f.idx[tm] = *(const SP24_LDS unsigned short*)(cur + lc.ldsM + tm * 16 * MB);
+          else f.idx[tm] = *(const SP24_LDS int*)(cur + lc.ldsM + tm * 16 * MB);
+        }
+      }
+      if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK) {
+        if (grp == 4) f.idxv[0] = *(const SP24_LDS i32x4*)(cur + lc.ldsM);
+        if constexpr (ES == 1)
+          if (grp == 6) f.idxv[1] = *(const SP24_LDS i32x4*)(cur + lc.ldsM + 16);
       }
     }
   };
@@ -373,8 +392,19 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   auto mfma_phase = [&](const DmaStep& d) {
 #pragma unroll
     for (int tm = 0; tm < 8; ++tm) {
+      if constexpr (LAYOUT == SP24_LAYOUT_ROW) {
 #pragma unroll
-      for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = smfmac16<OP>(acc[tm][tn], f.a[tm], f.b[tn], f.idx[tm]);
+        for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = smfmac16<OP>(acc[tm][tn], f.a[tm], f.b[tn], f.idx[tm]);
+      } else if constexpr (ES == 2) {  // word tm sits in half tm%2 of register tm/2
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) {
+          if (tm & 1) acc[tm][tn] = smfmac16<OP, 1>(acc[tm][tn], f.a[tm], f.b[tn], f.idxv[0][tm >> 1]);
+          else acc[tm][tn] = smfmac16<OP, 0>(acc[tm][tn], f.a[tm], f.b[tn], f.idxv[0][tm >> 1]);
+        }
+      } else {
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = smfmac16<OP>(acc[tm][tn], f.a[tm], f.b[tn], f.idxv[tm >> 2][tm & 3]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (tm == 0) dma_piece<OP, LAYOUT, 0>(d, lc, w);
       if (tm == 1) dma_piece<OP, LAYOUT, 2>(d, lc, w);
@@ -486,6 +516,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
   const int nt = (N + 15) >> 4;
   const int nsteps = (K + KS - 1) / KS;
   const int64_t rowA = (int64_t)K / 2 * ES, rowM = (int64_t)K / 8;
+  const int64_t Mp = ((int64_t)M + 127) / 128 * 128;  // KBLOCK metadata rows per block
   const int ldb = N * ES;                 // bytes per B row (multiple of 16)
   const int chunks_per_row = ldb >> 4;
   const int slice_instr = (KS * ldb) >> 10;  // 1 KiB per DMA instruction (KS*ldb is a multiple of 1 KiB)
@@ -499,10 +530,15 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
     if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK) {
       const int64_t blk = (int64_t)ks * M + m0;
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(A_vals + blk * 64, (uint64_t)(M - m0) * 64);
-      const __amdgpu_buffer_rsrc_t rm = make_rsrc(meta + blk * MB, (uint64_t)(M - m0) * MB);
+      // the metadata of rows m0 .. m0+15: row tile t of its 128-row group
+      const int64_t grp0 = (int64_t)ks * Mp + (m0 & ~127);
+      const int t = (m0 & 127) >> 4, r = l & 15;
+      const __amdgpu_buffer_rsrc_t rm = make_rsrc(meta + grp0 * MB, (uint64_t)128 * MB);
       a = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(valid ? (uint32_t)((l & 15) * 64 + 16 * ga) : kOOB), 0, 0);
-      if constexpr (ES == 2) idx = (int)__builtin_amdgcn_raw_buffer_load_b16(rm, (l & 15) * 8 + 2 * ga, 0, 0);
-      else idx = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, (l & 15) * 16 + 4 * ga, 0, 0);
+      if constexpr (ES == 2)
+        idx = (int)__builtin_amdgcn_raw_buffer_load_b16(rm, ((((r * 4 + ga) * 4 + (t >> 1)) * 2) + (t & 1)) * 2, 0, 0);
+      else
+        idx = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, ((r * 4 + ga) * 8 + t) * 4, 0, 0);
     } else {
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(A_vals + (int64_t)m0 * rowA, (uint64_t)(M - m0) * rowA);
       const __amdgpu_buffer_rsrc_t rm = make_rsrc(meta + (int64_t)m0 * rowM, (uint64_t)(M - m0) * rowM);

@@ -1,11 +1,19 @@
 """Test helper: the K-blocked compressed layout restated from include/sp24.h.
 
 Converts the oracle's row-major compressed output (M x K/2 values, M x K/32
-metadata words) into the K-blocked layout: K is cut into blocks of KB dense
-columns (64 for 16-bit types, 128 for 8-bit ones), block b of every row is
-stored together (values [b, i, :] = row i's KB/2 compressed values of block
-b; metadata [b, i, :] = its KB/32 words), and the tail of a partial last
-block is zero.  Pure data movement: no arithmetic of the method.
+metadata words) into the K-blocked layout.  K is cut into blocks of KB dense
+columns (64 for 16-bit types, 128 for 8-bit ones) and block b of every row
+is stored together; the tail of a partial last block is zero.
+
+  values    [b, i, :] = row i's KB/2 compressed values of block b;
+  metadata  per block, rows padded to Mp (a multiple of 128, zero codes);
+            a row's codes for the block are 4 words c_0..c_3 (16 bits each
+            for 16-bit types, 32 bits for 8-bit types, consecutive pieces of
+            its row-major words); inside a 128-row group, the word c_g of row
+            16t + r sits at u16 index ((r*4 + g)*4 + t//2)*2 + t%2 (16-bit)
+            or u32 index (r*4 + g)*8 + t (8-bit).
+
+Pure data movement: no arithmetic of the method.
 """
 import numpy as np
 
@@ -23,8 +31,17 @@ def row_to_kblock(vals, meta, dtype):
     VE, W = KB // 2, KB // 32
     v = np.zeros((M, nblk * VE), vals.dtype)
     v[:, :KC] = vals
-    m = np.zeros((M, nblk * W), np.uint32)
-    m[:, :meta.shape[1]] = meta
     v = np.ascontiguousarray(v.reshape(M, nblk, VE).transpose(1, 0, 2))
-    m = np.ascontiguousarray(m.reshape(M, nblk, W).transpose(1, 0, 2))
-    return v, m
+    Mp = -(-M // 128) * 128
+    m = np.zeros((Mp, nblk * W), np.uint32)
+    m[:M, :meta.shape[1]] = meta
+    m = m.reshape(Mp, nblk, W).transpose(1, 0, 2)  # [b][row][W words]
+    P = Mp // 128
+    if wl.ESIZE[dtype] == 2:
+        words = np.ascontiguousarray(m).view(np.uint16).reshape(nblk, P, 8, 16, 4)  # [b][p][t][r][g]
+        out = words.transpose(0, 1, 3, 4, 2).reshape(nblk, P, 16, 4, 4, 2)          # [b][p][r][g][t//2][t%2]
+        out = np.ascontiguousarray(out).reshape(nblk, Mp * 4).view(np.uint32)
+    else:
+        words = np.ascontiguousarray(m).reshape(nblk, P, 8, 16, 4)                  # [b][p][t][r][g]
+        out = np.ascontiguousarray(words.transpose(0, 1, 3, 4, 2)).reshape(nblk, Mp * 4)
+    return v, np.ascontiguousarray(out).reshape(nblk, Mp, W)

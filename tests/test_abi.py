@@ -38,13 +38,15 @@ def test_size_queries(L):
     assert L.sp24_values_bytes(8192, 8192, L.SP24_F16, ROW) == 8192 * 4096 * 2
     assert L.sp24_values_bytes(8192, 16384, L.SP24_FP8_E4M3, ROW) == 8192 * 8192
     assert L.sp24_meta_bytes(8192, 8192, L.SP24_F16, ROW) == 8192 * 8192 // 8
-    # K-blocked: whole blocks of 64 B values and 8 / 16 B metadata per row
+    # K-blocked: whole blocks of 64 B values per row, and 8 / 16 B of metadata
+    # per row with the rows padded to a multiple of 128
     assert L.sp24_values_bytes(8192, 8192, L.SP24_F16, KB) == 8192 * 4096 * 2
     assert L.sp24_meta_bytes(8192, 8192, L.SP24_F16, KB) == 8192 * 8192 // 8
     assert L.sp24_values_bytes(10, 96, L.SP24_BF16, KB) == 2 * 10 * 64       # 96 = 1.5 blocks of 64
-    assert L.sp24_meta_bytes(10, 96, L.SP24_BF16, KB) == 2 * 10 * 8
+    assert L.sp24_meta_bytes(10, 96, L.SP24_BF16, KB) == 2 * 128 * 8
     assert L.sp24_values_bytes(10, 160, L.SP24_I8, KB) == 2 * 10 * 64        # 160 = 1.25 blocks of 128
-    assert L.sp24_meta_bytes(10, 160, L.SP24_I8, KB) == 2 * 10 * 16
+    assert L.sp24_meta_bytes(10, 160, L.SP24_I8, KB) == 2 * 128 * 16
+    assert L.sp24_meta_bytes(129, 64, L.SP24_F16, KB) == 1 * 256 * 8
     assert L.sp24_values_bytes(4, 64, 99, ROW) == 0
     assert L.sp24_values_bytes(4, 64, L.SP24_F16, 7) == 0
     assert L.sp24_gemm_workspace_bytes(8192, 8192, 8192, L.SP24_F16, L.SP24_F16) == 0
@@ -83,6 +85,8 @@ def test_prune_compress_argument_errors(L):
     assert f(P, 2 * P, 3 * P, 4, 64, L.SP24_F16, 2, None) == 2                  # unknown layout
     # K-blocked values of 4 rows x 96 columns take 2 blocks = 512 B: meta right after 256 B overlaps
     assert f(P, 2 * P, 2 * P + 256, 4, 96, L.SP24_F16, L.SP24_LAYOUT_KBLOCK, None) == 1
+    # its metadata takes 2 blocks x 128 padded rows x 8 B = 2 KiB: values 1 KiB after it overlap
+    assert f(P, 3 * P + 1024, 3 * P, 4, 96, L.SP24_F16, L.SP24_LAYOUT_KBLOCK, None) == 1
 
 
 def test_gemm_argument_errors(L):
