@@ -494,122 +494,200 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
 }
 
 // ----------------------------------------------------------------------------
-// Small-N kernel (N <= 64): A is read from HBM exactly once.  A workgroup of
-// 8 waves owns one 16-row tile and all N columns; the waves split the
-// k-steps round-robin, each staging its own B slice (KS x N) through LDS for
-// the transpose reads, and the 8 partial tiles are summed on chip in a fixed
+// Small-N kernel (N <= 64): bound by HBM (A is read once, B is small and stays
+// in L2).  A workgroup of 8 waves owns one 16-row tile and all N columns; the
+// waves take the k-steps round-robin (wave w: steps w, w+8, ...).  Each wave
+// keeps D of its steps in flight in its own LDS ring: a slot holds the step's
+// A values (16 rows x 64 B, chunk-swizzled), the 16 rows' idx words (256 B)
+// and the B slice (KS rows x N).  All three arrive by direct-to-LDS loads,
+// issued through inline assembly and waited for with explicit vmcnt counts;
+// loads past the wave's last step read nothing, so every step issues the
+// same number of loads.  The 8 partial tiles are summed on chip in a fixed
 // order (deterministic).
+//   D = 4 when the B slice is at most 2 KiB (N <= 16), else 2 (N <= 64).
 // ----------------------------------------------------------------------------
 constexpr int kSmallWaves = 8;
-constexpr int kSmallBSlice = 64 * 64 * 2;  // KS * N * esize bytes, N <= 64
+constexpr int kSmallA = 1024, kSmallM = 256;
 
-template <int OP, int LAYOUT>
+template <int D>
+__host__ __device__ constexpr int small_bslice() { return D == 4 ? 2048 : 8192; }
+template <int D>
+__host__ __device__ constexpr int small_slot() { return kSmallA + kSmallM + small_bslice<D>(); }
+
+// s_waitcnt vmcnt(n) for a run-time n <= 15.
+__device__ __forceinline__ void wait_vm_upto15(int n) {
+  switch (n) {
+    case 0: waitcnt<0>(); break;
+    case 1: waitcnt<1>(); break;
+    case 2: waitcnt<2>(); break;
+    case 3: waitcnt<3>(); break;
+    case 4: waitcnt<4>(); break;
+    case 5: waitcnt<5>(); break;
+    case 6: waitcnt<6>(); break;
+    case 7: waitcnt<7>(); break;
+    case 8: waitcnt<8>(); break;
+    case 9: waitcnt<9>(); break;
+    case 10: waitcnt<10>(); break;
+    case 11: waitcnt<11>(); break;
+    case 12: waitcnt<12>(); break;
+    case 13: waitcnt<13>(); break;
+    case 14: waitcnt<14>(); break;
+    default: waitcnt<15>(); break;
+  }
+}
+
+template <int OP, int LAYOUT, int D>
 __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const char* __restrict__ A_vals,
                                                                         const char* __restrict__ meta,
                                                                         const char* __restrict__ B, void* C, int M,
                                                                         int N, int K, float alpha, float beta) {
   constexpr int KS = op_kstep(OP), ES = op_esize(OP), MB = meta_step_bytes<OP>();
-  __shared__ __attribute__((aligned(1024))) char lB[kSmallWaves][2][kSmallBSlice];
-  const int w = threadIdx.x >> 6, l = lane_id();
+  constexpr int SLOT = small_slot<D>();
+  __shared__ __attribute__((aligned(1024))) char lB[kSmallWaves * D * SLOT];
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), l = lane_id();
   const int m0 = blockIdx.x * 16;
   const int ga = l >> 4, gb = l >> 4, s = l & 15;
   const int nt = (N + 15) >> 4;
   const int nsteps = (K + KS - 1) / KS;
+  const int nw = nsteps > w ? (nsteps - w + kSmallWaves - 1) / kSmallWaves : 0;  // this wave's steps
   const int64_t rowA = (int64_t)K / 2 * ES, rowM = (int64_t)K / 8;
   const int64_t Mp = ((int64_t)M + 127) / 128 * 128;  // KBLOCK metadata rows per block
-  const int ldb = N * ES;                 // bytes per B row (multiple of 16)
+  const int ldb = N * ES;                              // bytes per B row (multiple of 16)
   const int chunks_per_row = ldb >> 4;
-  const int slice_instr = (KS * ldb) >> 10;  // 1 KiB per DMA instruction (KS*ldb is a multiple of 1 KiB)
+  const int slice_instr = (KS * ldb) >> 10;            // 1 KiB per load (KS*ldb is a multiple of 1 KiB)
+  const int LPS = 2 + slice_instr;                     // loads per step
   const int64_t btotal = (int64_t)K * ldb;
+  const int t16 = (m0 & 127) >> 4;                     // KBLOCK: row tile of the tile inside its 128-row group
+  SP24_LDS char* ring = (SP24_LDS char*)lB + w * D * SLOT;
+
+  // Per-lane load offsets, computed once (the loop only adds scalar step
+  // offsets).  A: lane l -> row l/4, chunk (l%4) ^ swzA(row).  idx: lane
+  // l = (row r = l/4, word g = l%4) -> the dword holding word g of row m0+r
+  // (K-blocked: inside the tile's 128-row group, for row tile t16; row-major:
+  // for 16-bit types the dword holding the u16 word g).  B: 1 KiB per load,
+  // lane l of load q -> chunk 64q + l of the slice.
+  const int a_row = l >> 2, a_ch = (l & 3) ^ swzA(l >> 2);
+  const int m_r = l >> 2, m_g = l & 3;
+  const uint32_t offA = LAYOUT == SP24_LAYOUT_KBLOCK ? (uint32_t)(a_row * 64 + 16 * a_ch)
+                                                     : (uint32_t)(a_row * rowA + 16 * a_ch);
+  uint32_t offM;
+  if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK)
+    offM = ES == 2 ? (uint32_t)(((m_r * 4 + m_g) * 4 + (t16 >> 1)) * 4) : (uint32_t)(((m_r * 4 + m_g) * 8 + t16) * 4);
+  else
+    offM = (uint32_t)(m_r * rowM + (ES == 2 ? 4 * (m_g >> 1) : 4 * m_g));
+  uint32_t offB[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int c = q * 64 + l;
+    const int brow = c / chunks_per_row, bc = c - brow * chunks_per_row;
+    offB[q] = (uint32_t)(brow * ldb + 16 * bc);
+  }
+  const int nfull = K / KS;
+  const i32x4 raRow = make_rsrc4(A_vals + (int64_t)m0 * rowA, (uint64_t)(M - m0) * rowA);
+  const i32x4 rmRow = make_rsrc4(meta + (int64_t)m0 * rowM, (uint64_t)(M - m0) * rowM);
+
+  // Every workgroup reads all of B; so that the workgroups in flight do not
+  // all ask for the same few B lines at once, each one starts its waves'
+  // step lists at a different point (a fixed rotation per workgroup: the
+  // summation order, and so the result, does not depend on timing).
+  const int rot = nw > 0 ? (int)(blockIdx.x % (unsigned)nw) : 0;
+
+  // Loads of this wave's local step j (global step w + 8*((j + rot) % nw))
+  // into ring slot u.  Local steps past nw get empty buffer ranges (nothing
+  // is read); in the step that ends past K the lanes past the row end are
+  // masked.
+  auto issue = [&](int j, int u) {
+    const bool in = j < nw;
+    const int jr = j + rot >= nw ? j + rot - nw : j + rot;
+    const int ks = w + kSmallWaves * (in ? jr : j);
+    const uint32_t la = lds_addr(ring + u * SLOT);
+    uint32_t oa, om;
+    i32x4 ra, rm;
+    if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK) {
+      ra = make_rsrc4(A_vals + ((int64_t)ks * M + m0) * 64, in ? (uint64_t)(M - m0) * 64 : 0u);
+      rm = make_rsrc4(meta + ((int64_t)ks * Mp + (m0 & ~127)) * MB, in ? (uint64_t)128 * MB : 0u);
+      oa = offA;
+      om = offM;
+    } else {
+      ra = raRow;
+      rm = rmRow;
+      oa = in ? offA + (uint32_t)(ks * 64) : kOOB;
+      om = in ? offM + (uint32_t)(ks * MB) : kOOB;
+    }
+    if (ks >= nfull && in) {  // the partial last step: mask what lies past K
+      if (16 * a_ch >= rowA - (int64_t)ks * 64) oa = kOOB;
+      if constexpr (LAYOUT == SP24_LAYOUT_ROW)
+        if ((int64_t)ks * MB + (ES == 2 ? 4 * (m_g >> 1) : 4 * m_g) >= rowM) om = kOOB;
+    }
+    dma16_asm(ra, la, oa, 0u);
+    dma4_asm(rm, la + kSmallA, om, 0u);
+    const int64_t start = (int64_t)ks * KS * ldb;
+    const i32x4 rb = make_rsrc4(B + start, (in && start < btotal) ? (uint64_t)(btotal - start) : 0u);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q < slice_instr) dma16_asm(rb, la + kSmallA + kSmallM + q * 1024, offB[q], 0u);
+  };
 
   i32x4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-  // Register prefetch of A and idx, LDS double buffer of the B slice.  A
-  // chunks past the row end (the K tail) are masked to zero.
-  auto fetch = [&](int ks, int buf, i32x4& a, int& idx) {
-    const bool valid = 16 * ga < rowA - (int64_t)ks * 64;
-    if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK) {
-      const int64_t blk = (int64_t)ks * M + m0;
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(A_vals + blk * 64, (uint64_t)(M - m0) * 64);
-      // the metadata of rows m0 .. m0+15: row tile t of its 128-row group
-      const int64_t grp0 = (int64_t)ks * Mp + (m0 & ~127);
-      const int t = (m0 & 127) >> 4, r = l & 15;
-      const __amdgpu_buffer_rsrc_t rm = make_rsrc(meta + grp0 * MB, (uint64_t)128 * MB);
-      a = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(valid ? (uint32_t)((l & 15) * 64 + 16 * ga) : kOOB), 0, 0);
-      if constexpr (ES == 2)
-        idx = (int)__builtin_amdgcn_raw_buffer_load_b16(rm, ((((r * 4 + ga) * 4 + (t >> 1)) * 2) + (t & 1)) * 2, 0, 0);
-      else
-        idx = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, ((r * 4 + ga) * 8 + t) * 4, 0, 0);
-    } else {
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(A_vals + (int64_t)m0 * rowA, (uint64_t)(M - m0) * rowA);
-      const __amdgpu_buffer_rsrc_t rm = make_rsrc(meta + (int64_t)m0 * rowM, (uint64_t)(M - m0) * rowM);
-      const uint32_t offa = valid ? (uint32_t)((l & 15) * rowA + (int64_t)ks * 64 + 16 * ga) : kOOB;
-      a = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)offa, 0, 0);
-      if constexpr (ES == 2)
-        idx = (int)__builtin_amdgcn_raw_buffer_load_b16(rm, (int)((l & 15) * rowM + ks * 8 + 2 * ga), 0, 0);
-      else
-        idx = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, (int)((l & 15) * rowM + ks * 16 + 4 * ga), 0, 0);
-    }
-    const int64_t start = (int64_t)ks * KS * ldb;
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + start, btotal - start);
-    for (int j = 0; j < slice_instr; ++j) {
-      const int q = j * 64 + l;  // chunk index inside the slice
-      const int brow = q / chunks_per_row, bc = q - brow * chunks_per_row;
-      dma16(rb, (SP24_LDS char*)lB[w][buf] + j * 1024, (uint32_t)(brow * ldb + 16 * bc));
-    }
-  };
-  i32x4 a_cur, a_nxt;
-  int i_cur = 0, i_nxt = 0;
-  int ks = w, buf = 0;
-  if (ks < nsteps) fetch(ks, 0, a_cur, i_cur);
-  for (; ks < nsteps; ks += kSmallWaves) {
-    const int ksn = ks + kSmallWaves;
-    if (ksn < nsteps) fetch(ksn, buf ^ 1, a_nxt, i_nxt);
-    // wait for everything except the prefetch just issued
-    if (ksn < nsteps) {
-      switch (slice_instr) {  // the prefetch is 2 + slice_instr loads
-        case 1: waitcnt<3>(); break;
-        case 2: waitcnt<4>(); break;
-        case 3: waitcnt<5>(); break;
-        case 4: waitcnt<6>(); break;
-        case 5: waitcnt<7>(); break;
-        case 6: waitcnt<8>(); break;
-        case 7: waitcnt<9>(); break;
-        default: waitcnt<10>(); break;
-      }
-    } else {
-      waitcnt<0>();
-    }
-    const SP24_LDS char* sb = (const SP24_LDS char*)lB[w][buf];
-    for (int tn = 0; tn < nt; ++tn) {
+  // One step from ring slot u.
+  auto compute = [&](int u) {
+    const SP24_LDS char* slot = ring + u * SLOT;
+    const i32x4 a = *(const SP24_LDS i32x4*)(slot + s * 64 + 16 * (ga ^ swzA(s)));
+    int idx = *(const SP24_LDS int*)(slot + kSmallA + 4 * (s * 4 + ga));
+    if constexpr (LAYOUT == SP24_LAYOUT_ROW && ES == 2) idx = (int)((uint32_t)idx >> (16 * (ga & 1)));
+    const SP24_LDS char* sb = slot + kSmallA + kSmallM;
+    // (unrolled with a guard: a run-time index into the accumulators would
+    // turn into indirect register addressing)
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      if (tn >= nt) break;
       i32x2 p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (ES == 2) {
           const int k = 8 * gb + 4 * (r & 1) + 32 * (r >> 1) + (s >> 2);
-          const int addr = k * ldb + tn * 32 + (s & 3) * 8;
-          p[r] = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((SP24_LDS i16x4*)(sb + addr)));
+          p[r] = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                               (SP24_LDS i16x4*)(sb + k * ldb + tn * 32 + (s & 3) * 8)));
         } else {
           const int k = 16 * gb + 8 * (r & 1) + 64 * (r >> 1) + (s >> 1);
-          const int addr = k * ldb + tn * 16 + (s & 1) * 8;
-          p[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SP24_LDS i32x2*)(sb + addr));
+          p[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SP24_LDS i32x2*)(sb + k * ldb + tn * 16 + (s & 1) * 8));
         }
       }
       const i32x8 b = {p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
-      acc[tn] = smfmac16<OP>(acc[tn], a_cur, b, i_cur);
+      // K-blocked 16-bit idx: the tile's word sits in half t16%2 of the dword
+      if (LAYOUT == SP24_LAYOUT_KBLOCK && ES == 2 && (t16 & 1)) acc[tn] = smfmac16<OP, 1>(acc[tn], a, b, idx);
+      else acc[tn] = smfmac16<OP, 0>(acc[tn], a, b, idx);
     }
-    a_cur = a_nxt;
-    i_cur = i_nxt;
-    buf ^= 1;
+  };
+
+#pragma unroll
+  for (int u = 0; u < D; ++u) issue(u, u);
+  for (int j = 0; j < nw; j += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      if (j + u >= nw) break;
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm_upto15((D - 1) * LPS);  // local step j+u has landed (the D-1 later ones may still be in flight)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      compute(u);
+      waitcnt<63, 0>();  // this slot's reads are done before it is refilled
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      issue(j + u + D, u);
+    }
   }
   // ---- reduce the 8 partial tiles in LDS (fixed order), then epilogue
   waitcnt<0, 0>();
   __syncthreads();
-  int* red = (int*)&lB[0][0][0];  // 8 waves x 4 tiles x 64 lanes x 4 regs x 4 B = 32 KiB
-  for (int tn = 0; tn < nt; ++tn)
+  int* red = (int*)&lB[0];  // 8 waves x 4 tiles x 64 lanes x 4 regs x 4 B = 32 KiB
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn) {
+    if (tn >= nt) break;
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[((w * 4 + tn) * 4 + r) * 64 + l] = acc[tn][r];
+  }
   __syncthreads();
-  // thread t handles output element (i, j) = (t / 64 .. ) of the 16 x N tile
   for (int e = threadIdx.x; e < 16 * nt * 16; e += kSmallWaves * 64) {
     const int tn = e >> 8, within = e & 255;
     const int i = within >> 4, j = within & 15;
@@ -620,14 +698,14 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
     if constexpr (op_is_int(OP)) {
       int sum = 0;
       for (int ww = 0; ww < kSmallWaves; ++ww) sum += red[((ww * 4 + tn) * 4 + r) * 64 + lane];
-      int* D = static_cast<int*>(C);
-      D[o] = beta != 0.0f ? sum + D[o] : sum;
+      int* Dp = static_cast<int*>(C);
+      Dp[o] = beta != 0.0f ? sum + Dp[o] : sum;
     } else {
       float sum = 0.0f;
       for (int ww = 0; ww < kSmallWaves; ++ww) sum += __int_as_float(red[((ww * 4 + tn) * 4 + r) * 64 + lane]);
-      float* D = static_cast<float*>(C);
+      float* Dp = static_cast<float*>(C);
       const float v = alpha * sum;
-      D[o] = beta != 0.0f ? v + beta * D[o] : v;
+      Dp[o] = beta != 0.0f ? v + beta * Dp[o] : v;
     }
   }
 }
@@ -659,8 +737,11 @@ static hipError_t launch_op(const void* A_vals, const uint32_t* meta, const void
     return hipGetLastError();
   }
   if (N <= 64) {
-    hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT>), dim3((unsigned)((M + 15) / 16)), dim3(kSmallWaves * 64), 0,
-                       stream, a, m, b, C, M, N, K, alpha, beta);
+    const dim3 grid((unsigned)((M + 15) / 16)), block(kSmallWaves * 64);
+    if ((int64_t)op_kstep(OP) * N * op_esize(OP) <= small_bslice<4>())
+      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 4>), grid, block, 0, stream, a, m, b, C, M, N, K, alpha, beta);
+    else
+      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 2>), grid, block, 0, stream, a, m, b, C, M, N, K, alpha, beta);
     return hipGetLastError();
   }
   const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
