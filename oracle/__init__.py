@@ -57,6 +57,8 @@ def _load():
         lib.orc_key.restype = ctypes.c_uint32
         lib.orc_prune_compress.argtypes = [P, P, P, I64, I64, I]
         lib.orc_decompress.argtypes = [P, P, P, I64, I64, I]
+        lib.orc_count_invalid.argtypes = [P, I64, I64]
+        lib.orc_count_invalid.restype = I64
         lib.orc_gemm_f64.argtypes = [P, P, I, P, I, P, P, P, I64, I64, I64, D, D]
         lib.orc_gemm_i64.argtypes = [P, P, P, P, P, I64, I64, I64, I]
         lib.orc_gemm_points_f64.argtypes = [P, P, I, P, I, P, I64, I64, I64, D, D, I64, P, P, P, P]
@@ -127,6 +129,16 @@ def decompress(vals, meta, dtype):
     out = np.empty((M, K), dtype=_STORE[dtype])
     _check(lib.orc_decompress(_ptr(vals), _ptr(meta), _ptr(out), M, K, dtype), "decompress")
     return out
+
+
+def count_invalid(meta, K):
+    """Number of groups of the M x K/32 metadata whose codes are not strictly increasing."""
+    lib = _load()
+    meta = np.ascontiguousarray(meta, dtype=np.uint32)
+    n = lib.orc_count_invalid(_ptr(meta), meta.shape[0], K)
+    if n < 0:
+        raise ValueError("count_invalid: bad arguments")
+    return int(n)
 
 
 def gemm_f64(vals, meta, a_type, B, b_type, C=None, alpha=1.0, beta=0.0, want_abs=True):

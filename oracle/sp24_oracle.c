@@ -186,6 +186,19 @@ int orc_decompress(const void* vals, const uint32_t* meta, void* A, int64_t M, i
   return ORC_OK;
 }
 
+/* Number of groups whose two codes are not strictly increasing (p0 >= p1):
+ * metadata that compression never produces and that the product's hardware
+ * form leaves undefined.  Plain count over rows and groups. */
+int64_t orc_count_invalid(const uint32_t* meta, int64_t M, int64_t K) {
+  if (M < 0 || K < 0 || K % 32 != 0) return -1;
+  const int64_t KW = K / 32;
+  int64_t bad = 0;
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t g = 0; g < K / 4; ++g)
+      if (code_of(meta, KW, i, 2 * g) >= code_of(meta, KW, i, 2 * g + 1)) ++bad;
+  return bad;
+}
+
 static double* decode_table(int dtype) {
   const int esz = orc_elem_size(dtype);
   const int n = esz == 2 ? 65536 : 256;

@@ -292,3 +292,28 @@ def test_epilogue_special_cases(orc):
 def test_bad_arguments_rejected(orc):
     with pytest.raises(ValueError):
         orc.prune_compress(np.zeros((4, 48), np.uint16), wl.F16)   # K not a multiple of 32
+
+
+# ---- metadata validity count and decompression of invalid codes ---------------
+def test_count_invalid_pins(orc):
+    """Invalid = the two codes of a group are not strictly increasing."""
+    assert orc.count_invalid(np.full((3, 4), 0x88888888, np.uint32), 128) == 0
+    assert orc.count_invalid(np.zeros((5, 2), np.uint32), 64) == 5 * 16      # every code 0: all groups bad
+    # brute force over the 16 code pairs of group 3 in a word whose other groups are (0, 2)
+    for c0 in range(4):
+        for c1 in range(4):
+            w = 0x88888888 & ~(0xF << 12) | (c0 << 12) | (c1 << 14)
+            assert orc.count_invalid(np.array([[w]], np.uint32), 32) == int(c0 >= c1)
+    # compression never produces invalid metadata
+    A = wl.random_case(4, 33, 16, 256, wl.F16, wl.F16).A
+    _, meta = orc.prune_compress(A, wl.F16)
+    assert orc.count_invalid(meta, 256) == 0
+
+
+def test_decompress_invalid_codes_second_value_wins(orc):
+    """With both codes of a group naming the same slot, that slot holds the second value."""
+    vals = np.zeros((1, 16), np.uint16)
+    vals[0, 0], vals[0, 1] = 0x3C00, 0x4000  # 1.0 and 2.0
+    meta = np.array([[0x88888888 & ~0xF | (2 | 2 << 2)]], np.uint32)  # group 0: codes (2, 2)
+    d = orc.decompress(vals, meta, wl.F16)
+    assert d[0, 2] == 0x4000 and d[0, 0] == 0 and d[0, 1] == 0 and d[0, 3] == 0
