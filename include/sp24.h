@@ -170,6 +170,40 @@ int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, 
               int64_t M, int64_t N, int64_t K, float alpha, float beta, void* workspace,
               size_t workspace_bytes, void* stream);
 
+/*
+ * sp24_decompress -- (A_vals, meta) -> dense A, the inverse of compression:
+ * in every group of 4 the two stored values go to the positions their codes
+ * name and the other two elements become +0 (all-zero bits) ("CDNA and CDNA2
+ * sparse MFMA builtins", section "Structured sparsity (4:2 pattern)").  If
+ * both codes of a group name one position (metadata compression never
+ * produces), the group's second value is left there.
+ *
+ *   A_vals, meta  in: compressed A in `layout` (sizes as for
+ *                 sp24_prune_compress).
+ *   A             out: M x K elements of `dtype`, row-major.
+ * Errors: INVALID_VALUE (shape, null pointer, A overlapping an input),
+ * UNSUPPORTED (dtype or layout), MISALIGNED, LAUNCH.
+ */
+int sp24_decompress(const void* A_vals, const uint32_t* meta, void* A, int64_t M, int64_t K, int dtype, int layout,
+                    void* stream);
+
+/*
+ * sp24_validate_meta -- counts the groups whose two codes are not strictly
+ * increasing (p0 >= p1).  sp24_prune_compress never produces such groups;
+ * sp24_gemm gives unspecified results for them, so callers that build
+ * metadata themselves can check it here first.  Only the M rows and the K
+ * columns are examined (not the K-blocked padding).
+ *
+ *   meta        in: metadata of an M x K matrix of `dtype` in `layout`.
+ *   bad_groups  out: DEVICE pointer to one uint64 (8-byte aligned), set to
+ *               the count when the stream reaches this call (the library
+ *               clears it with a kernel of its own, no memset).
+ * Errors: INVALID_VALUE (shape, null pointer, overlap), UNSUPPORTED,
+ * MISALIGNED (meta not 16-byte or bad_groups not 8-byte aligned), LAUNCH.
+ */
+int sp24_validate_meta(const uint32_t* meta, int64_t M, int64_t K, int dtype, int layout, uint64_t* bad_groups,
+                       void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* sp24_status_string(int status);
 

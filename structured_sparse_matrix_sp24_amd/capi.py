@@ -47,6 +47,10 @@ def lib():
         L.sp24_prune_compress.restype = I
         L.sp24_gemm.argtypes = [P, P, I, I, P, I, P, I64, I64, I64, F, F, P, SZ, P]
         L.sp24_gemm.restype = I
+        L.sp24_decompress.argtypes = [P, P, P, I64, I64, I, I, P]
+        L.sp24_decompress.restype = I
+        L.sp24_validate_meta.argtypes = [P, I64, I64, I, I, P, P]
+        L.sp24_validate_meta.restype = I
         L.sp24_status_string.argtypes = [I]
         L.sp24_status_string.restype = ctypes.c_char_p
         L.sp24_version.argtypes = []
@@ -78,6 +82,16 @@ def sp24_gemm(A_vals: int, meta: int, a_type: int, layout: int, B: int, b_type: 
               stream: int | None) -> int:
     return lib().sp24_gemm(A_vals, meta, a_type, layout, B, b_type, C, M, N, K, alpha, beta, workspace,
                            workspace_bytes, stream)
+
+
+def sp24_decompress(A_vals: int, meta: int, A: int, M: int, K: int, dtype: int, layout: int,
+                    stream: int | None) -> int:
+    return lib().sp24_decompress(A_vals, meta, A, M, K, dtype, layout, stream)
+
+
+def sp24_validate_meta(meta: int, M: int, K: int, dtype: int, layout: int, bad_groups: int,
+                       stream: int | None) -> int:
+    return lib().sp24_validate_meta(meta, M, K, dtype, layout, bad_groups, stream)
 
 
 def sp24_status_string(status: int) -> str:
@@ -182,3 +196,34 @@ def gemm(A_vals, meta, B, C=None, alpha: float = 1.0, beta: float = 0.0, a_type:
     if st != SP24_OK:
         raise Sp24Error(st, "sp24_gemm")
     return C
+
+
+def decompress(A_vals, meta, K: int, dtype: int | None = None, layout: int | None = None, stream=None):
+    """Dense M x K tensor (same element type as A_vals) from compressed A.
+    ``layout`` defaults to what the tensors' rank says: 2-D = ROW, 3-D = KBLOCK."""
+    import torch
+    if dtype is None:
+        dtype = dtype_code(A_vals.dtype)
+    if layout is None:
+        layout = SP24_LAYOUT_KBLOCK if A_vals.dim() == 3 else SP24_LAYOUT_ROW
+    M = A_vals.shape[0] if layout == SP24_LAYOUT_ROW else A_vals.shape[1]
+    vshape, mshape = compressed_shapes(M, K, dtype, layout)
+    if tuple(A_vals.shape) != vshape or tuple(meta.shape) != mshape:
+        raise ValueError(f"compressed A has shapes {tuple(A_vals.shape)} / {tuple(meta.shape)}; "
+                         f"K = {K} in this layout needs {vshape} / {mshape}")
+    A = torch.empty((M, K), dtype=A_vals.dtype, device=A_vals.device)
+    st = sp24_decompress(A_vals.data_ptr(), meta.data_ptr(), A.data_ptr(), M, K, dtype, layout, _stream(stream))
+    if st != SP24_OK:
+        raise Sp24Error(st, "sp24_decompress")
+    return A
+
+
+def validate_meta(meta, M: int, K: int, dtype: int, layout: int, stream=None):
+    """Number of groups whose two codes are not strictly increasing (a device
+    int64 tensor of one element, filled when the stream reaches the call)."""
+    import torch
+    out = torch.empty(1, dtype=torch.int64, device=meta.device)
+    st = sp24_validate_meta(meta.data_ptr(), M, K, dtype, layout, out.data_ptr(), _stream(stream))
+    if st != SP24_OK:
+        raise Sp24Error(st, "sp24_validate_meta")
+    return out

@@ -9,6 +9,10 @@ hipError_t launch_prune_compress(const void* A, void* vals, uint32_t* meta, int6
                                  int layout, hipStream_t stream);
 hipError_t launch_gemm(int op, int layout, const void* A_vals, const uint32_t* meta, const void* B, void* C, int M,
                        int N, int K, float alpha, float beta, hipStream_t stream);
+hipError_t launch_decompress(const void* vals, const uint32_t* meta, void* A, int64_t M, int64_t K, int dtype,
+                             int layout, hipStream_t stream);
+hipError_t launch_validate(const uint32_t* meta, int64_t M, int64_t K, int dtype, int layout, uint64_t* bad,
+                           hipStream_t stream);
 }  // namespace sp24
 
 namespace {
@@ -124,6 +128,34 @@ int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, 
   return e == hipSuccess ? SP24_OK : SP24_ERR_LAUNCH;
 }
 
+int sp24_decompress(const void* A_vals, const uint32_t* meta, void* A, int64_t M, int64_t K, int dtype, int layout,
+                    void* stream) {
+  const int es = esize(dtype);
+  if (es == 0 || !layout_ok(layout)) return SP24_ERR_UNSUPPORTED;
+  if (M < 0 || K < 0 || K % 32 != 0 || M > kMaxDim || K > kMaxDim) return SP24_ERR_INVALID_VALUE;
+  if (M == 0 || K == 0) return SP24_OK;
+  if (!A || !A_vals || !meta) return SP24_ERR_INVALID_VALUE;
+  if (!aligned16(A) || !aligned16(A_vals) || !aligned16(meta)) return SP24_ERR_MISALIGNED;
+  const uint64_t a_bytes = (uint64_t)M * K * es;
+  const uint64_t v_bytes = sp24_values_bytes(M, K, dtype, layout), m_bytes = sp24_meta_bytes(M, K, dtype, layout);
+  if (overlap(A, a_bytes, A_vals, v_bytes) || overlap(A, a_bytes, meta, m_bytes)) return SP24_ERR_INVALID_VALUE;
+  const hipError_t e = sp24::launch_decompress(A_vals, meta, A, M, K, dtype, layout, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SP24_OK : SP24_ERR_LAUNCH;
+}
+
+int sp24_validate_meta(const uint32_t* meta, int64_t M, int64_t K, int dtype, int layout, uint64_t* bad_groups,
+                       void* stream) {
+  const int es = esize(dtype);
+  if (es == 0 || !layout_ok(layout)) return SP24_ERR_UNSUPPORTED;
+  if (M < 0 || K < 0 || K % 32 != 0 || M > kMaxDim || K > kMaxDim) return SP24_ERR_INVALID_VALUE;
+  if (!bad_groups || (M > 0 && K > 0 && !meta)) return SP24_ERR_INVALID_VALUE;
+  if ((reinterpret_cast<uintptr_t>(bad_groups) & 7u) != 0 || (meta && !aligned16(meta))) return SP24_ERR_MISALIGNED;
+  if (meta && overlap(bad_groups, 8, meta, sp24_meta_bytes(M, K, dtype, layout))) return SP24_ERR_INVALID_VALUE;
+  const hipError_t e =
+      sp24::launch_validate(meta, M, K, dtype, layout, bad_groups, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SP24_OK : SP24_ERR_LAUNCH;
+}
+
 const char* sp24_status_string(int status) {
   switch (status) {
     case SP24_OK: return "SP24_OK";
@@ -135,6 +167,6 @@ const char* sp24_status_string(int status) {
   }
 }
 
-int sp24_version(void) { return 200; }
+int sp24_version(void) { return 300; }
 
 }  // extern "C"

@@ -1,0 +1,210 @@
+// sp24_decompress / sp24_validate_meta: the inverse of compression and a
+// check of compressed metadata, both bound by HBM bandwidth (no MFMA, no LDS).
+//
+// Decompression restores the dense row from its kept values and their 2-bit
+// positions: each group of four gets its two values at the positions its
+// codes name, the other two elements are +0 ("CDNA and CDNA2 sparse MFMA
+// builtins", section "Structured sparsity (4:2 pattern)").  Codes that name
+// the same position twice (never produced by compression) leave the second
+// value there.
+//
+// Validation counts the groups whose two codes are not strictly increasing:
+// compression never produces them, and the matrix-core product leaves them
+// undefined, so a caller can check metadata built by other means.
+#include "sp24_internal.hpp"
+
+namespace sp24 {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecUnroll = 4;
+
+// One group of four 16-bit values from its two kept values and 4-bit code
+// (p0 in bits 0-1, p1 in bits 2-3); the second value wins a shared slot.
+__device__ __forceinline__ uint64_t expand16(uint32_t pair, uint32_t nib) {
+  const uint32_t p0 = nib & 3u, p1 = (nib >> 2) & 3u;
+  uint64_t w = (uint64_t)(pair & 0xFFFFu) << (16 * p0);
+  w &= ~(0xFFFFull << (16 * p1));
+  return w | ((uint64_t)(pair >> 16) << (16 * p1));
+}
+// The same for four 8-bit values.
+__device__ __forceinline__ uint32_t expand8(uint32_t pair, uint32_t nib) {
+  const uint32_t p0 = nib & 3u, p1 = (nib >> 2) & 3u;
+  uint32_t w = (pair & 0xFFu) << (8 * p0);
+  w &= ~(0xFFu << (8 * p1));
+  return w | (((pair >> 8) & 0xFFu) << (8 * p1));
+}
+
+// 8 bytes of values + the chunk's codes -> one 16-byte chunk of dense A.
+template <int ES>
+__device__ __forceinline__ i32x4 expand_chunk(i32x2 v, uint32_t code) {
+  i32x4 out;
+  if constexpr (ES == 2) {
+    const uint64_t g0 = expand16((uint32_t)v[0], code & 0xFu);
+    const uint64_t g1 = expand16((uint32_t)v[1], (code >> 4) & 0xFu);
+    out = i32x4{(int)(uint32_t)g0, (int)(uint32_t)(g0 >> 32), (int)(uint32_t)g1, (int)(uint32_t)(g1 >> 32)};
+  } else {
+    out = i32x4{(int)expand8((uint32_t)v[0] & 0xFFFFu, code & 0xFu),
+                (int)expand8((uint32_t)v[0] >> 16, (code >> 4) & 0xFu),
+                (int)expand8((uint32_t)v[1] & 0xFFFFu, (code >> 8) & 0xFu),
+                (int)expand8((uint32_t)v[1] >> 16, (code >> 12) & 0xFu)};
+  }
+  return out;
+}
+
+// Row-major layout: chunk q of A (16 bytes) <- 8 bytes of values at q and the
+// codes at metadata byte q (16-bit) or bytes 2q, 2q+1 (8-bit), independent of
+// M and K because K % 32 == 0.
+template <int ES>
+__global__ __launch_bounds__(kDecThreads) void decompress_row_kernel(const i32x2* __restrict__ vals,
+                                                                       const uint8_t* __restrict__ meta,
+                                                                       i32x4* __restrict__ A, int64_t nchunks) {
+  const int64_t base = (int64_t)blockIdx.x * (kDecThreads * kDecUnroll) + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kDecUnroll; ++u) {
+    const int64_t q = base + (int64_t)u * kDecThreads;
+    if (q >= nchunks) break;
+    const i32x2 v = __builtin_nontemporal_load(vals + q);
+    const uint32_t code = ES == 2 ? (uint32_t)meta[q] : (uint32_t)reinterpret_cast<const uint16_t*>(meta)[q];
+    __builtin_nontemporal_store(expand_chunk<ES>(v, code), A + q);
+  }
+}
+
+// K-blocked layout: workgroup (row tile rt, block b) covers rows rt*128 ..
+// +128 of block b, thread t chunk t%8 of rows rt*128 + t/8 + 32u; the codes
+// are read from their interleaved position in the row's 128-row group.
+template <int ES>
+__global__ __launch_bounds__(kDecThreads) void decompress_kblock_kernel(const char* __restrict__ vals,
+                                                                          const char* __restrict__ meta,
+                                                                          char* __restrict__ A, int64_t M, int64_t K,
+                                                                          uint32_t nblk) {
+  constexpr int MB = ES == 2 ? 8 : 16, CE = 16 / ES;
+  const int64_t b = blockIdx.x % nblk;
+  const uint32_t rt = blockIdx.x / nblk;
+  const int64_t Mp = (M + 127) / 128 * 128;
+  const int c = threadIdx.x & 7;
+  const int64_t kcol = b * (8 * CE) + (int64_t)c * CE;
+  if (kcol >= K) return;
+  const char* mgroup = meta + (b * Mp + (int64_t)rt * 128) * MB;
+#pragma unroll
+  for (int u = 0; u < kDecUnroll; ++u) {
+    const int rr = (threadIdx.x >> 3) + 32 * u;
+    const int64_t row = (int64_t)rt * 128 + rr;
+    if (row >= M) break;
+    const int t = rr >> 4, r = rr & 15;
+    const i32x2 v = __builtin_nontemporal_load(reinterpret_cast<const i32x2*>(vals + (b * M + row) * 64 + c * 8));
+    uint32_t code;
+    if constexpr (ES == 2)
+      code = *reinterpret_cast<const uint8_t*>(mgroup + (((r * 4 + c / 2) * 4 + t / 2) * 2 + (t & 1)) * 2 + (c & 1));
+    else
+      code = *reinterpret_cast<const uint16_t*>(mgroup + ((r * 4 + c / 2) * 8 + t) * 4 + (c & 1) * 2);
+    __builtin_nontemporal_store(expand_chunk<ES>(v, code), reinterpret_cast<i32x4*>(A + row * K * ES + kcol * ES));
+  }
+}
+
+// ---- validation ---------------------------------------------------------------
+// Groups, among the first `ngroups` 4-bit codes of w, whose codes are not
+// strictly increasing (p0 >= p1).
+__device__ __forceinline__ int bad_groups_in(uint32_t w, int ngroups) {
+  int bad = 0;
+  for (int g = 0; g < ngroups; ++g) {
+    const uint32_t nib = (w >> (4 * g)) & 0xFu;
+    bad += (nib & 3u) >= ((nib >> 2) & 3u);
+  }
+  return bad;
+}
+
+// Sum over the wave, then one 64-bit vector atomic per wave.
+__device__ __forceinline__ void add_wave_count(int n, unsigned long long* out) {
+  for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off, 64);
+  if (lane_id() == 0 && n != 0) atomicAdd(out, (unsigned long long)n);
+}
+
+__global__ void zero_u64_kernel(unsigned long long* p) { *p = 0ull; }
+
+// Row-major layout: one 32-bit word (8 groups) per thread, grid-stride.
+__global__ __launch_bounds__(256) void validate_row_kernel(const uint32_t* __restrict__ meta, int64_t nwords,
+                                                            unsigned long long* out) {
+  int bad = 0;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nwords; q += (int64_t)gridDim.x * blockDim.x)
+    bad += bad_groups_in(meta[q], 8);
+  add_wave_count(bad, out);
+}
+
+// K-blocked layout: one code word (row i < M, word g) of one block per thread,
+// grid-stride; only groups inside K are counted (the tail of a partial last
+// block and the padding rows hold zero codes).
+template <int ES>
+__global__ __launch_bounds__(256) void validate_kblock_kernel(const char* __restrict__ meta, int64_t M, int64_t K,
+                                                               int64_t nblk, unsigned long long* out) {
+  constexpr int MB = ES == 2 ? 8 : 16, KB = ES == 2 ? 64 : 128, GPW = KB / 16;  // groups per word
+  const int64_t Mp = (M + 127) / 128 * 128;
+  const int64_t total = nblk * M * 4;
+  int bad = 0;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (int64_t)gridDim.x * blockDim.x) {
+    const int g = (int)(q & 3);
+    const int64_t i = (q >> 2) % M, b = (q >> 2) / M;
+    const int rr = (int)(i & 127), t = rr >> 4, r = rr & 15;
+    const char* mgroup = meta + (b * Mp + (i & ~127ll)) * MB;
+    uint32_t w;
+    if constexpr (ES == 2) w = *reinterpret_cast<const uint16_t*>(mgroup + (((r * 4 + g) * 4 + t / 2) * 2 + (t & 1)) * 2);
+    else w = *reinterpret_cast<const uint32_t*>(mgroup + ((r * 4 + g) * 8 + t) * 4);
+    const int64_t col0 = b * KB + (int64_t)g * (KB / 4);  // first dense column of the word
+    const int64_t inside = (K - col0) / 4;                // groups of the word inside K
+    bad += bad_groups_in(w, inside >= GPW ? GPW : (inside > 0 ? (int)inside : 0));
+  }
+  add_wave_count(bad, out);
+}
+
+// ---- host launchers (arguments already validated) ------------------------------
+hipError_t launch_decompress(const void* vals, const uint32_t* meta, void* A, int64_t M, int64_t K, int dtype,
+                             int layout, hipStream_t stream) {
+  const int es = (dtype == SP24_F16 || dtype == SP24_BF16) ? 2 : 1;
+  if (M == 0 || K == 0) return hipSuccess;
+  const dim3 block(kDecThreads);
+  if (layout == SP24_LAYOUT_KBLOCK) {
+    const int64_t kb = es == 2 ? 64 : 128;
+    const int64_t nblk = (K + kb - 1) / kb, row_tiles = (M + 127) / 128;
+    if (row_tiles * nblk > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(row_tiles * nblk));
+    const char* v = static_cast<const char*>(vals);
+    const char* m = reinterpret_cast<const char*>(meta);
+    char* a = static_cast<char*>(A);
+    if (es == 2) hipLaunchKernelGGL((decompress_kblock_kernel<2>), grid, block, 0, stream, v, m, a, M, K, (uint32_t)nblk);
+    else hipLaunchKernelGGL((decompress_kblock_kernel<1>), grid, block, 0, stream, v, m, a, M, K, (uint32_t)nblk);
+    return hipGetLastError();
+  }
+  const int64_t nchunks = M * K * es / 16;
+  const int64_t blocks = (nchunks + kDecThreads * kDecUnroll - 1) / (kDecThreads * kDecUnroll);
+  if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+  const i32x2* v = static_cast<const i32x2*>(vals);
+  const uint8_t* m = reinterpret_cast<const uint8_t*>(meta);
+  i32x4* a = static_cast<i32x4*>(A);
+  if (es == 2) hipLaunchKernelGGL((decompress_row_kernel<2>), dim3((unsigned)blocks), block, 0, stream, v, m, a, nchunks);
+  else hipLaunchKernelGGL((decompress_row_kernel<1>), dim3((unsigned)blocks), block, 0, stream, v, m, a, nchunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_validate(const uint32_t* meta, int64_t M, int64_t K, int dtype, int layout, uint64_t* bad,
+                           hipStream_t stream) {
+  const int es = (dtype == SP24_F16 || dtype == SP24_BF16) ? 2 : 1;
+  unsigned long long* out = reinterpret_cast<unsigned long long*>(bad);
+  // cleared by a kernel (not a memset), so the call can be captured in a graph
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, stream, out);
+  if (M == 0 || K == 0) return hipGetLastError();
+  if (layout == SP24_LAYOUT_KBLOCK) {
+    const int64_t kb = es == 2 ? 64 : 128;
+    const int64_t nblk = (K + kb - 1) / kb;
+    const int64_t total = nblk * M * 4;
+    const unsigned grid = (unsigned)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+    const char* m = reinterpret_cast<const char*>(meta);
+    if (es == 2) hipLaunchKernelGGL((validate_kblock_kernel<2>), dim3(grid), dim3(256), 0, stream, m, M, K, nblk, out);
+    else hipLaunchKernelGGL((validate_kblock_kernel<1>), dim3(grid), dim3(256), 0, stream, m, M, K, nblk, out);
+    return hipGetLastError();
+  }
+  const int64_t nwords = M * (K / 32);
+  const unsigned grid = (unsigned)((nwords + 255) / 256 < 4096 ? (nwords + 255) / 256 : 4096);
+  hipLaunchKernelGGL(validate_row_kernel, dim3(grid), dim3(256), 0, stream, meta, nwords, out);
+  return hipGetLastError();
+}
+
+}  // namespace sp24

@@ -117,3 +117,18 @@ def test_gemm_argument_errors(L):
     # the row-major layout addresses a 256-row tile with 32-bit offsets: K is bounded
     big_k = 1 << 23
     assert L.sp24_gemm(A, Mt, F16, L.SP24_LAYOUT_ROW, B, F16, C, 64, 64, big_k, 1.0, 0.0, None, 0, None) == 2
+
+
+def test_decompress_and_validate_argument_errors(L):
+    d, v = L.sp24_decompress, L.sp24_validate_meta
+    KB, ROW, F16 = L.SP24_LAYOUT_KBLOCK, L.SP24_LAYOUT_ROW, L.SP24_F16
+    for lay in (ROW, KB):
+        assert d(P, 2 * P, 3 * P, 4, 48, F16, lay, None) == 1          # K % 32
+        assert d(P, 2 * P, 3 * P, 4, 64, 9, lay, None) == 2            # dtype
+        assert d(P, 2 * P, 3 * P + 8, 4, 64, F16, lay, None) == 3      # misaligned A
+        assert d(P, 2 * P, P + 64, 4, 64, F16, lay, None) == 1         # A overlaps A_vals
+        assert d(0, 0, 0, 0, 64, F16, lay, None) == 0                  # empty
+        assert v(P, 4, 64, F16, lay, 0, None) == 1                     # null counter
+        assert v(P, 4, 64, F16, lay, 2 * P + 4, None) == 3             # counter not 8-byte aligned
+        assert v(P, 4, 48, F16, lay, 2 * P, None) == 1                 # K % 32
+        assert v(P, 4, 64, F16, 7, 2 * P, None) == 2                   # layout

@@ -299,3 +299,57 @@ def test_workload_full_size(pkg, name):
         check_gemm_full(pkg, ov, om, w.a_type, w.B, w.b_type, w.C, w.alpha, w.beta)
     else:
         check_gemm_sampled(D, ov, om, w)
+
+
+# ---- decompression and metadata validation -------------------------------------------
+def _rand_meta(seed, M, K):
+    """Random code words: every code value, valid and invalid groups alike."""
+    g = np.random.default_rng(seed)
+    return g.integers(0, 2 ** 32, (M, K // 32), dtype=np.uint64).astype(np.uint32)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16, wl.I8, wl.E4M3, wl.E5M2])
+@pytest.mark.parametrize("shape", [(1, 32), (129, 160), (300, 4096), (64, 96)])
+def test_decompress_matches_oracle(pkg, dtype, shape, layout):
+    M, K = shape
+    _say(f"decompress dtype={dtype} M={M} K={K} layout={layout}")
+    c = wl.random_case(17, M, 16, K, dtype, dtype)
+    ov, om = oracle.prune_compress(c.A, dtype)
+    for vals, meta in ((ov, om), (ov, _rand_meta(5, M, K))):  # compressor output, then arbitrary codes
+        ev, em = in_layout(vals, meta, dtype, layout)
+        V = to_dev(ev, dtype)
+        Mt = torch.from_numpy(np.ascontiguousarray(em).view(np.int32)).to(DEV)
+        D = pkg.decompress(V, Mt, K, dtype, layout)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(D, dtype), oracle.decompress(vals, meta, dtype))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("dtype", [wl.F16, wl.I8])
+@pytest.mark.parametrize("shape", [(1, 32), (129, 160), (300, 4096), (70, 96)])
+def test_validate_meta_counts_like_oracle(pkg, dtype, shape, layout):
+    M, K = shape
+    _say(f"validate dtype={dtype} M={M} K={K} layout={layout}")
+    vals = np.zeros((M, K // 2), wl.STORE[dtype])
+    for meta, expect in ((_rand_meta(9, M, K), None), (np.full((M, K // 32), 0x88888888, np.uint32), 0)):
+        _, em = in_layout(vals, meta, dtype, layout)
+        Mt = torch.from_numpy(np.ascontiguousarray(em).view(np.int32)).to(DEV)
+        n = int(pkg.validate_meta(Mt, M, K, dtype, layout).item())
+        ref = oracle.count_invalid(meta, K)
+        assert n == ref
+        if expect is not None:
+            assert n == expect
+
+
+def test_gpu_compress_then_decompress_is_prune(pkg):
+    """decompress(compress(A)) on the GPU equals the oracle's pruned A."""
+    c = wl.random_case(23, 257, 16, 352, wl.BF16, wl.BF16)
+    A = to_dev(c.A, wl.BF16)
+    for layout in LAYOUTS:
+        V, Mt = pkg.prune_compress(A, layout=layout)
+        D = pkg.decompress(V, Mt, 352, layout=layout)
+        assert int(pkg.validate_meta(Mt, 257, 352, wl.BF16, layout).item()) == 0
+        torch.cuda.synchronize()
+        ov, om = oracle.prune_compress(c.A, wl.BF16)
+        assert np.array_equal(to_host_bits(D, wl.BF16), oracle.decompress(ov, om, wl.BF16))
