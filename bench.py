@@ -51,11 +51,18 @@ def src_hash(*rel):
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload, kernel_src_hash):
+def traffic_name(workload, layout, b_layout):
+    """Stem of the profiles/ files for a run: the workload, plus the layouts
+    when they are not the defaults (kblock, kn)."""
+    extra = "" if (layout, b_layout) == ("kblock", "kn") else f"_{layout}_{b_layout}"
+    return f"{workload}{extra}"
+
+
+def load_traffic(name, kernel_src_hash):
     """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE),
     scaled by the same counters' reading for a plain copy of known size.
     Returned only if taken on the current kernel source."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    p = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -114,6 +121,8 @@ def main():
     ap.add_argument("--workload", default="f16_8192", choices=sorted(WORKLOADS))
     ap.add_argument("--layout", default="kblock", choices=["kblock", "row"],
                     help="compressed layout the step writes and the GEMM reads")
+    ap.add_argument("--b-layout", default="kn", choices=["kn", "nk"],
+                    help="how B is stored: K x N (kn) or transposed, N x K (nk, e.g. activations)")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the oracle sample (default: sized to ~15 s)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--gemm-only-launches", type=int, default=0,
@@ -156,6 +165,9 @@ def main():
 
     A = up(w.A, w.a_type)
     B = up(w.B, w.b_type)
+    b_layout = {"kn": pkg.SP24_B_KN, "nk": pkg.SP24_B_NK}[args.b_layout]
+    if b_layout == pkg.SP24_B_NK:  # the same B, stored transposed (set-up, not timed)
+        B = B.t().contiguous()
     out_dtype = torch.int32 if w.a_type == wl.I8 else torch.float32
     C = torch.from_numpy(w.C).to(dev) if w.C is not None else torch.empty((w.M, w.N), dtype=out_dtype, device=dev)
     C0 = C.clone() if w.beta != 0.0 else None
@@ -173,7 +185,7 @@ def main():
             raise pkg.Sp24Error(st, "sp24_prune_compress")
 
     def gemm():
-        st = pkg.sp24_gemm(vals.data_ptr(), meta.data_ptr(), w.a_type, layout, B.data_ptr(), w.b_type,
+        st = pkg.sp24_gemm(vals.data_ptr(), meta.data_ptr(), w.a_type, layout, B.data_ptr(), w.b_type, b_layout,
                            C.data_ptr(), w.M, w.N, w.K, w.alpha, w.beta, None, 0, sh)
         if st:
             raise pkg.Sp24Error(st, "sp24_gemm")
@@ -224,16 +236,17 @@ def main():
     gemm_gbps = gemm_bytes / (gemm_ms * 1e-3) / 1e9
     khash = src_hash("structured_sparse_matrix_sp24_amd/csrc/sp24_gemm.hip",
                      "structured_sparse_matrix_sp24_amd/csrc/sp24_internal.hpp")
+    traffic = load_traffic(traffic_name(args.workload, args.layout, args.b_layout), khash)
     hbm_bound = w.N <= 64
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(gemm_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(gemm_gbps / PEAK_HBM_GBPS, 4), "traffic": load_traffic(args.workload, khash),
+                "frac": round(gemm_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
                 "kernel": "sp24 gemm (small-N)", "kernel_ms": round(gemm_ms, 5),
                 "algorithmic_bytes": gemm_bytes}
     else:
         peak = PEAK_SPARSE_TFLOPS[label]
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(gemm_tflops / peak, 4), "traffic": load_traffic(args.workload, khash),
+                "frac": round(gemm_tflops / peak, 4), "traffic": traffic,
                 "kernel": "sp24 gemm (256x256 tile)", "kernel_ms": round(gemm_ms, 5),
                 "algorithmic_flop": flop}
     res = {
@@ -252,6 +265,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "M": w.M, "N": w.N, "K": w.K, "a_type": wl_name(w.a_type),
                    "b_type": wl_name(w.b_type), "alpha": w.alpha, "beta": w.beta, "layout": args.layout,
+                   "b_layout": args.b_layout,
                    "step": "sp24_prune_compress(A) + sp24_gemm(A_vals, meta, B, C)"},
         "gemm_tflops": round(gemm_tflops, 1),
         "gemm_frac_sparse_peak": round(gemm_tflops / PEAK_SPARSE_TFLOPS[label], 4),

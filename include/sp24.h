@@ -15,7 +15,9 @@
  *
  * Dense layouts (row-major, dense leading dimensions, no padding):
  *   A       M x K elements of the input type, K contiguous.
- *   B       K x N elements, N contiguous.  K is the dense K.
+ *   B       SP24_B_KN: K x N elements, N contiguous (the default);
+ *           SP24_B_NK: stored as N x K elements, K contiguous (B transposed,
+ *           e.g. the activations of a linear layer).  K is the dense K.
  *   C / D   M x N float32 (int32 when both inputs are int8), updated in place.
  *
  * Compressed layouts (sp24_layout).  In both, the 2-bit code (0..3, position
@@ -89,6 +91,11 @@ typedef enum {
 } sp24_layout;
 
 typedef enum {
+  SP24_B_KN = 0,
+  SP24_B_NK = 1
+} sp24_b_layout;
+
+typedef enum {
   SP24_OK = 0,
   SP24_ERR_INVALID_VALUE = 1, /* bad shape, null pointer, overlap, workspace too small */
   SP24_ERR_UNSUPPORTED = 2,   /* type pair, alpha/beta or leading dimension not supported */
@@ -151,23 +158,25 @@ int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, 
  *                 layout; codes are trusted -- a group whose two codes are
  *                 not strictly increasing gives unspecified results).
  *   a_type        element type of A_vals; b_type element type of B.
- *   B             K x N elements of b_type.
+ *   B             K x N elements of b_type (SP24_B_KN) or its transpose,
+ *                 N x K (SP24_B_NK), as `b_layout` says.
  *   C             in/out: M x N float32 (int32 for int8 x int8).  Not read
  *                 when beta == 0 (NaN there does not propagate).
  *   M, N, K       >= 0, K % 32 == 0, N * sizeof(b_type) % 16 == 0,
  *                 N * sizeof(b_type) <= 16 MiB - 2 (so 128 rows of B stay
- *                 below 2 GiB) and, for the ROW layout, 256 * K/2 *
- *                 sizeof(a_type) < 2 GiB (K <= 8388606 for 16-bit types).
+ *                 below 2 GiB), for SP24_B_NK 256 * K * sizeof(b_type) <
+ *                 2 GiB and, for the ROW layout, 256 * K/2 * sizeof(a_type)
+ *                 < 2 GiB (K <= 8388606 for 16-bit types).
  *                 M == 0 or N == 0: nothing is enqueued.  K == 0: D = beta*C.
  *   alpha, beta   float scalars.  For int8: alpha must be 1, beta 0 or 1.
  *   workspace     may be NULL when sp24_gemm_workspace_bytes() == 0.
  * Errors: INVALID_VALUE (shape, null pointer, C overlapping an input,
  * workspace too small), UNSUPPORTED (type pair, int8 alpha/beta, N*size not a
- * multiple of 16 bytes, N or K past the limits above, unknown layout),
- * MISALIGNED, LAUNCH.
+ * multiple of 16 bytes, N or K past the limits above, unknown layout or
+ * b_layout), MISALIGNED, LAUNCH.
  */
-int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, const void* B, int b_type, void* C,
-              int64_t M, int64_t N, int64_t K, float alpha, float beta, void* workspace,
+int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, const void* B, int b_type,
+              int b_layout, void* C, int64_t M, int64_t N, int64_t K, float alpha, float beta, void* workspace,
               size_t workspace_bytes, void* stream);
 
 /*

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libsp24.so")
 
 SP24_F16, SP24_BF16, SP24_I8, SP24_FP8_E4M3, SP24_BF8_E5M2 = 1, 2, 3, 4, 5
 SP24_LAYOUT_ROW, SP24_LAYOUT_KBLOCK = 0, 1
+SP24_B_KN, SP24_B_NK = 0, 1
 SP24_OK = 0
 _ESIZE = {SP24_F16: 2, SP24_BF16: 2, SP24_I8: 1, SP24_FP8_E4M3: 1, SP24_BF8_E5M2: 1}
 
@@ -45,7 +46,7 @@ def lib():
         L.sp24_gemm_workspace_bytes.restype = SZ
         L.sp24_prune_compress.argtypes = [P, P, P, I64, I64, I, I, P]
         L.sp24_prune_compress.restype = I
-        L.sp24_gemm.argtypes = [P, P, I, I, P, I, P, I64, I64, I64, F, F, P, SZ, P]
+        L.sp24_gemm.argtypes = [P, P, I, I, P, I, I, P, I64, I64, I64, F, F, P, SZ, P]
         L.sp24_gemm.restype = I
         L.sp24_decompress.argtypes = [P, P, P, I64, I64, I, I, P]
         L.sp24_decompress.restype = I
@@ -77,10 +78,10 @@ def sp24_prune_compress(A: int, A_vals: int, meta: int, M: int, K: int, dtype: i
     return lib().sp24_prune_compress(A, A_vals, meta, M, K, dtype, layout, stream)
 
 
-def sp24_gemm(A_vals: int, meta: int, a_type: int, layout: int, B: int, b_type: int, C: int, M: int, N: int,
-              K: int, alpha: float, beta: float, workspace: int | None, workspace_bytes: int,
+def sp24_gemm(A_vals: int, meta: int, a_type: int, layout: int, B: int, b_type: int, b_layout: int, C: int, M: int,
+              N: int, K: int, alpha: float, beta: float, workspace: int | None, workspace_bytes: int,
               stream: int | None) -> int:
-    return lib().sp24_gemm(A_vals, meta, a_type, layout, B, b_type, C, M, N, K, alpha, beta, workspace,
+    return lib().sp24_gemm(A_vals, meta, a_type, layout, B, b_type, b_layout, C, M, N, K, alpha, beta, workspace,
                            workspace_bytes, stream)
 
 
@@ -169,6 +170,8 @@ def gemm(A_vals, meta, B, C=None, alpha: float = 1.0, beta: float = 0.0, a_type:
     """D = alpha * expand(A_vals, meta) @ B + beta * C, written into C
     (allocated, uninitialised, when C is None and beta == 0).  ``layout``
     defaults to what the tensors' rank says: 2-D = ROW, 3-D = KBLOCK.
+    B is K x N: either contiguous (SP24_B_KN) or the transpose of a
+    contiguous N x K tensor, e.g. ``X.t()`` for activations X (SP24_B_NK).
     Returns C."""
     import torch
     if a_type is None:
@@ -178,6 +181,12 @@ def gemm(A_vals, meta, B, C=None, alpha: float = 1.0, beta: float = 0.0, a_type:
     if layout is None:
         layout = SP24_LAYOUT_KBLOCK if A_vals.dim() == 3 else SP24_LAYOUT_ROW
     K, N = B.shape
+    if B.is_contiguous():
+        b_layout = SP24_B_KN
+    elif B.t().is_contiguous():
+        b_layout = SP24_B_NK
+    else:
+        raise ValueError("B must be contiguous or the transpose of a contiguous tensor")
     M = A_vals.shape[0] if layout == SP24_LAYOUT_ROW else A_vals.shape[1]
     vshape, mshape = compressed_shapes(M, K, a_type, layout)
     if tuple(A_vals.shape) != vshape or tuple(meta.shape) != mshape:
@@ -188,11 +197,11 @@ def gemm(A_vals, meta, B, C=None, alpha: float = 1.0, beta: float = 0.0, a_type:
         if beta != 0.0:
             raise ValueError("beta != 0 needs C")
         C = torch.empty((M, N), dtype=out_dtype, device=B.device)
-    for t in (A_vals, meta, B, C):
+    for t in (A_vals, meta, C):
         if not t.is_contiguous():
-            raise ValueError("all operands must be contiguous")
-    st = sp24_gemm(A_vals.data_ptr(), meta.data_ptr(), a_type, layout, B.data_ptr(), b_type, C.data_ptr(), M, N, K,
-                   float(alpha), float(beta), None, 0, _stream(stream))
+            raise ValueError("A_vals, meta and C must be contiguous")
+    st = sp24_gemm(A_vals.data_ptr(), meta.data_ptr(), a_type, layout, B.data_ptr(), b_type, b_layout, C.data_ptr(),
+                   M, N, K, float(alpha), float(beta), None, 0, _stream(stream))
     if st != SP24_OK:
         raise Sp24Error(st, "sp24_gemm")
     return C

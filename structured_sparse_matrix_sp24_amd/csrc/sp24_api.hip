@@ -7,8 +7,8 @@
 namespace sp24 {
 hipError_t launch_prune_compress(const void* A, void* vals, uint32_t* meta, int64_t M, int64_t K, int dtype,
                                  int layout, hipStream_t stream);
-hipError_t launch_gemm(int op, int layout, const void* A_vals, const uint32_t* meta, const void* B, void* C, int M,
-                       int N, int K, float alpha, float beta, hipStream_t stream);
+hipError_t launch_gemm(int op, int layout, int b_layout, const void* A_vals, const uint32_t* meta, const void* B,
+                       void* C, int M, int N, int K, float alpha, float beta, hipStream_t stream);
 hipError_t launch_decompress(const void* vals, const uint32_t* meta, void* A, int64_t M, int64_t K, int dtype,
                              int layout, hipStream_t stream);
 hipError_t launch_validate(const uint32_t* meta, int64_t M, int64_t K, int dtype, int layout, uint64_t* bad,
@@ -96,11 +96,11 @@ int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, 
   return e == hipSuccess ? SP24_OK : SP24_ERR_LAUNCH;
 }
 
-int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, const void* B, int b_type, void* C,
-              int64_t M, int64_t N, int64_t K, float alpha, float beta, void* workspace, size_t workspace_bytes,
-              void* stream) {
+int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, const void* B, int b_type,
+              int b_layout, void* C, int64_t M, int64_t N, int64_t K, float alpha, float beta, void* workspace,
+              size_t workspace_bytes, void* stream) {
   const int op = op_for(a_type, b_type);
-  if (op < 0 || !layout_ok(layout)) return SP24_ERR_UNSUPPORTED;
+  if (op < 0 || !layout_ok(layout) || (b_layout != SP24_B_KN && b_layout != SP24_B_NK)) return SP24_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
     return SP24_ERR_INVALID_VALUE;
   const int ea = esize(a_type), eb = esize(b_type);
@@ -110,6 +110,7 @@ int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, 
   // buffer ranges below 2 GiB.
   if ((uint64_t)N * eb * 128 > kTileBytesMax) return SP24_ERR_UNSUPPORTED;
   if (layout == SP24_LAYOUT_ROW && (uint64_t)(K / 2) * ea * 256 > kTileBytesMax) return SP24_ERR_UNSUPPORTED;
+  if (b_layout == SP24_B_NK && (uint64_t)K * eb * 256 > kTileBytesMax) return SP24_ERR_UNSUPPORTED;
   if (op == sp24::OP_I8 && (alpha != 1.0f || (beta != 0.0f && beta != 1.0f))) return SP24_ERR_UNSUPPORTED;
   if (workspace_bytes < sp24_gemm_workspace_bytes(M, N, K, a_type, b_type)) return SP24_ERR_INVALID_VALUE;
   (void)workspace;
@@ -123,8 +124,8 @@ int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, 
                 overlap(C, c_bytes, meta, sp24_meta_bytes(M, K, a_type, layout)) ||
                 overlap(C, c_bytes, B, (uint64_t)K * N * eb)))
     return SP24_ERR_INVALID_VALUE;
-  const hipError_t e = sp24::launch_gemm(op, layout, A_vals, meta, B, C, (int)M, (int)N, (int)K, alpha, beta,
-                                         static_cast<hipStream_t>(stream));
+  const hipError_t e = sp24::launch_gemm(op, layout, b_layout, A_vals, meta, B, C, (int)M, (int)N, (int)K, alpha,
+                                         beta, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SP24_OK : SP24_ERR_LAUNCH;
 }
 

@@ -24,7 +24,10 @@
 //   16-bit:  k in [8gb, 8gb+8)  and [32+8gb, 32+8gb+8)      (KS = 64)
 //   8-bit:   k in [16gb, 16gb+16) and [64+16gb, 64+16gb+16) (KS = 128)
 // which the LDS transpose reads (ds_read_b64_tr_b16 / _b8) deliver 4 or 8 k
-// at a time from a row-major (k, n) tile.
+// at a time from a row-major (k, n) tile.  When B is stored transposed
+// (N x K, sp24_b_layout SP24_B_NK) one k-step of a column is 128 contiguous
+// bytes, both runs are 16-byte chunks of it (chunks gb and gb+4), and two
+// plain 16-byte LDS reads fetch a fragment.
 #include <type_traits>
 
 #include "sp24_internal.hpp"
@@ -90,6 +93,10 @@ __device__ __forceinline__ int swzA(int r) { return ((r >> 2) & 1) | ((((r >> 1)
 // a lane's read address is a per-lane constant plus immediates.
 __device__ __forceinline__ int swzB16(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
 __device__ __forceinline__ int swzB8(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
+// Transposed B (N x K): LDS row n holds the step's 128 bytes of column n,
+// chunk c stored at c ^ swzBT(n).  16 lanes reading one chunk of 16
+// consecutive columns then cover all 64 banks once.
+__device__ __forceinline__ int swzBT(int n) { return (n >> 1) & 7; }
 
 // Load instructions per wave per k-step: A 2, B 4, metadata 1 (16-bit) or 2.
 template <int OP>
@@ -102,10 +109,13 @@ struct LaneConsts8 {
   uint32_t voM[2];  // metadata: rows 32w .. +32 of the tile
   int ldsA;         // A fragment read offset
   int ldsM;         // idx read offset (inside the stage)
-  int ldsB[4];      // B transpose-read base of each column tile
+  int ldsB[4];      // K x N: transpose-read base of each column tile;
+                    // N x K: [0], [1] the two chunks of column tile 0
+  int chB[4];       // N x K: chunk of the step each B load lane fetches
 };
 
-template <int OP, int LAYOUT>
+// ldb: bytes per row of B as stored (N * esize for K x N, K * esize for N x K).
+template <int OP, int LAYOUT, int BL>
 __device__ __forceinline__ LaneConsts8 make_lane_consts8(int w, int l, int64_t rowA, int64_t rowM, int ldb) {
   constexpr int ES = op_esize(OP), MB = meta_step_bytes<OP>();
   constexpr bool KB = LAYOUT == SP24_LAYOUT_KBLOCK;
@@ -119,7 +129,11 @@ __device__ __forceinline__ LaneConsts8 make_lane_consts8(int w, int l, int64_t r
   for (int i = 0; i < 4; ++i) {
     const int j = w * 4 + i;
     int row, ch;
-    if constexpr (ES == 2) {
+    if constexpr (BL == SP24_B_NK) {  // columns 8j .. 8j+8, 8 lanes per column
+      row = j * 8 + (l >> 3);
+      ch = (l & 7) ^ swzBT(row);
+      c.chB[i] = ch;
+    } else if constexpr (ES == 2) {
       row = j * 2 + (l >> 5);
       const int p = l & 31;
       ch = (((p >> 1) ^ swzB16(row)) << 1) | (p & 1);
@@ -146,6 +160,12 @@ __device__ __forceinline__ LaneConsts8 make_lane_consts8(int w, int l, int64_t r
   else               // [row][MB]
     c.ldsM = kLdsA + kLdsB + (wm * 128 + r16) * MB + (ES == 2 ? 2 * ga : 4 * ga);
   const int gb = l >> 4, s = l & 15;
+  if constexpr (BL == SP24_B_NK) {
+    const int n = wn * 64 + s;  // swzBT(n + 16 tn) == swzBT(n)
+    c.ldsB[0] = kLdsA + n * 128 + 16 * (gb ^ swzBT(n));
+    c.ldsB[1] = kLdsA + n * 128 + 16 * ((gb + 4) ^ swzBT(n));
+    return c;
+  }
 #pragma unroll
   for (int tn = 0; tn < 4; ++tn) {
     const int ct = wn * 4 + tn;
@@ -181,6 +201,7 @@ struct TileArgs {
   int64_t rowA;    // compressed bytes per row (ROW stride; both: K tail)
   int64_t rowM;    // metadata bytes per row (ROW stride; both: K tail)
   int64_t btotal;  // bytes of B
+  int64_t ldbk;    // N x K: bytes per row of B
   int M, N, m0, n0, nsteps, nfull;
   int Mp;          // KBLOCK: metadata rows per block (M rounded up to 128)
 };
@@ -198,9 +219,10 @@ struct DmaStep {
   bool tail;         // the step ends past K (masking needed)
   int64_t validA;    // bytes of the step inside a row of A
   int64_t validM;    // ROW layout: bytes of the step inside a metadata row
+  int64_t validB;    // N x K: bytes of the step inside a row of B
 };
 
-template <int OP, int LAYOUT>
+template <int OP, int LAYOUT, int BL>
 __device__ __forceinline__ DmaStep make_dma_step(SP24_LDS char* st, const TileArgs& ta, int j) {
   constexpr int KS = op_kstep(OP), ES = op_esize(OP), MB = meta_step_bytes<OP>();
   DmaStep d;
@@ -219,8 +241,18 @@ __device__ __forceinline__ DmaStep make_dma_step(SP24_LDS char* st, const TileAr
     d.offA = (uint32_t)(j * 64);
     d.offM = (uint32_t)(j * MB);
   }
-  const int64_t start = ((int64_t)j * KS * ta.N + ta.n0) * ES;
-  d.rB = make_rsrc4(ta.B + start, start < ta.btotal ? (uint64_t)(ta.btotal - start) : 0u);
+  if constexpr (BL == SP24_B_NK) {
+    // the tile's columns from byte j*128 on: rows past N fall outside the
+    // range, the end of the row in the last step is masked per lane
+    d.validB = ta.ldbk - (int64_t)j * 128;
+    const int64_t rows = min(ta.N - ta.n0, kBN);
+    d.rB = make_rsrc4(ta.B + (int64_t)ta.n0 * ta.ldbk + (int64_t)j * 128,
+                      d.validB > 0 ? (uint64_t)(rows * ta.ldbk - (int64_t)j * 128) : 0u);
+  } else {
+    const int64_t start = ((int64_t)j * KS * ta.N + ta.n0) * ES;
+    d.rB = make_rsrc4(ta.B + start, start < ta.btotal ? (uint64_t)(ta.btotal - start) : 0u);
+    d.validB = 0;
+  }
   return d;
 }
 
@@ -230,7 +262,7 @@ __device__ __forceinline__ DmaStep make_dma_step(SP24_LDS char* st, const TileAr
 //   P = 6, 7   metadata piece P-6 (8-bit inputs load two, 16-bit one).
 // In a step that ends past K (the last one when K is not a multiple of KS,
 // and those past the end) lanes past the row end are masked.
-template <int OP, int LAYOUT, int P>
+template <int OP, int LAYOUT, int BL, int P>
 __device__ __forceinline__ void dma_piece(const DmaStep& d, const LaneConsts8& lc, int w) {
   constexpr int ES = op_esize(OP);
   if constexpr (P < 2) {
@@ -242,7 +274,10 @@ __device__ __forceinline__ void dma_piece(const DmaStep& d, const LaneConsts8& l
     }
     dma16_asm(d.rA, d.lds + (w * 2 + P) * 1024, off, 0u);
   } else if constexpr (P < 6) {
-    dma16_asm(d.rB, d.lds + kLdsA + (w * 4 + P - 2) * 1024, lc.voB[P - 2], 0u);
+    uint32_t off = lc.voB[P - 2];
+    if constexpr (BL == SP24_B_NK)
+      if (d.tail && 16 * lc.chB[P - 2] >= d.validB) off = kOOB;
+    dma16_asm(d.rB, d.lds + kLdsA + (w * 4 + P - 2) * 1024, off, 0u);
   } else {
     constexpr int i = P - 6;
     uint32_t off = lc.voM[i] + d.offM;
@@ -272,7 +307,7 @@ __device__ __forceinline__ void phase_end() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int OP, int LAYOUT>
+template <int OP, int LAYOUT, int BL>
 __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __restrict__ A_vals,
                                                                  const char* __restrict__ meta,
                                                                  const char* __restrict__ B, void* C, int M, int N,
@@ -311,6 +346,7 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   ta.rowA = (int64_t)K / 2 * ES;
   ta.rowM = (int64_t)K / 8;
   ta.btotal = (int64_t)K * N * ES;
+  ta.ldbk = (int64_t)K * ES;
   ta.M = M;
   ta.N = N;
   ta.m0 = m0;
@@ -324,7 +360,8 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   } else {
     ta.rA = ta.rM = i32x4{0, 0, 0, 0};
   }
-  const LaneConsts8 lc = make_lane_consts8<OP, LAYOUT>(w, l, ta.rowA, ta.rowM, N * ES);
+  const LaneConsts8 lc =
+      make_lane_consts8<OP, LAYOUT, BL>(w, l, ta.rowA, ta.rowM, BL == SP24_B_NK ? K * ES : N * ES);
   const int nsteps = ta.nsteps;
 
   i32x4 acc[8][4];
@@ -338,6 +375,12 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   // B tiles, groups 4-7 the A rows and their idx words.
   auto read_group = [&](const SP24_LDS char* cur, int grp) {
     if (grp < 4) {
+      if constexpr (BL == SP24_B_NK) {
+        const i32x4 lo = *(const SP24_LDS i32x4*)(cur + lc.ldsB[0] + grp * 2048);
+        const i32x4 hi = *(const SP24_LDS i32x4*)(cur + lc.ldsB[1] + grp * 2048);
+        f.b[grp] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return;
+      }
       const SP24_LDS char* p = cur + lc.ldsB[grp];
       i32x2 q[4];
       if constexpr (ES == 2) {
@@ -371,15 +414,15 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   };
   // All loads of this wave's share of step j, back to back (pipeline fill).
   auto dma_all = [&](int j) {
-    const DmaStep d = make_dma_step<OP, LAYOUT>(st(j % 3), ta, j);
-    dma_piece<OP, LAYOUT, 0>(d, lc, w);
-    dma_piece<OP, LAYOUT, 1>(d, lc, w);
-    dma_piece<OP, LAYOUT, 2>(d, lc, w);
-    dma_piece<OP, LAYOUT, 3>(d, lc, w);
-    dma_piece<OP, LAYOUT, 4>(d, lc, w);
-    dma_piece<OP, LAYOUT, 5>(d, lc, w);
-    dma_piece<OP, LAYOUT, 6>(d, lc, w);
-    if constexpr (L == 8) dma_piece<OP, LAYOUT, 7>(d, lc, w);
+    const DmaStep d = make_dma_step<OP, LAYOUT, BL>(st(j % 3), ta, j);
+    dma_piece<OP, LAYOUT, BL, 0>(d, lc, w);
+    dma_piece<OP, LAYOUT, BL, 1>(d, lc, w);
+    dma_piece<OP, LAYOUT, BL, 2>(d, lc, w);
+    dma_piece<OP, LAYOUT, BL, 3>(d, lc, w);
+    dma_piece<OP, LAYOUT, BL, 4>(d, lc, w);
+    dma_piece<OP, LAYOUT, BL, 5>(d, lc, w);
+    dma_piece<OP, LAYOUT, BL, 6>(d, lc, w);
+    if constexpr (L == 8) dma_piece<OP, LAYOUT, BL, 7>(d, lc, w);
   };
   // Staging phase: the fragments of step jr.
   auto stage_phase = [&](int jr) {
@@ -406,15 +449,15 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
         for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = smfmac16<OP>(acc[tm][tn], f.a[tm], f.b[tn], f.idxv[tm >> 2][tm & 3]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (tm == 0) dma_piece<OP, LAYOUT, 0>(d, lc, w);
-      if (tm == 1) dma_piece<OP, LAYOUT, 2>(d, lc, w);
-      if (tm == 2) dma_piece<OP, LAYOUT, 3>(d, lc, w);
-      if (tm == 3) dma_piece<OP, LAYOUT, 1>(d, lc, w);
-      if (tm == 4) dma_piece<OP, LAYOUT, 4>(d, lc, w);
-      if (tm == 5) dma_piece<OP, LAYOUT, 5>(d, lc, w);
-      if (tm == 6) dma_piece<OP, LAYOUT, 6>(d, lc, w);
+      if (tm == 0) dma_piece<OP, LAYOUT, BL, 0>(d, lc, w);
+      if (tm == 1) dma_piece<OP, LAYOUT, BL, 2>(d, lc, w);
+      if (tm == 2) dma_piece<OP, LAYOUT, BL, 3>(d, lc, w);
+      if (tm == 3) dma_piece<OP, LAYOUT, BL, 1>(d, lc, w);
+      if (tm == 4) dma_piece<OP, LAYOUT, BL, 4>(d, lc, w);
+      if (tm == 5) dma_piece<OP, LAYOUT, BL, 5>(d, lc, w);
+      if (tm == 6) dma_piece<OP, LAYOUT, BL, 6>(d, lc, w);
       if constexpr (L == 8)
-        if (tm == 7) dma_piece<OP, LAYOUT, 7>(d, lc, w);
+        if (tm == 7) dma_piece<OP, LAYOUT, BL, 7>(d, lc, w);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -431,12 +474,12 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   if (g0) {
     phase_end<L>();  // this wave's share of step 0 has landed
     stage_phase(0);
-    DmaStep d = make_dma_step<OP, LAYOUT>(st(2), ta, 2);
+    DmaStep d = make_dma_step<OP, LAYOUT, BL>(st(2), ta, 2);
     for (int k = 0; k < nsteps; ++k) {
       mfma_phase(d);              // phase 2k: step k, loads of step k+2
       phase_end<L>();             // this wave's share of step k+1 has landed
       stage_phase(k + 1);         // phase 2k+1
-      d = make_dma_step<OP, LAYOUT>(st((k + 3) % 3), ta, k + 3);
+      d = make_dma_step<OP, LAYOUT, BL>(st((k + 3) % 3), ta, k + 3);
       phase_end<63>();            // the reads of step k+1 are done
     }
   } else {
@@ -444,7 +487,7 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
     phase_end<2 * L>();
     for (int k = 0; k < nsteps; ++k) {
       stage_phase(k);             // phase 2k
-      const DmaStep d = make_dma_step<OP, LAYOUT>(st(k % 3), ta, k + 3);
+      const DmaStep d = make_dma_step<OP, LAYOUT, BL>(st(k % 3), ta, k + 3);
       phase_end<L>();             // this wave's share of step k+1 has landed, the reads of step k are done
       mfma_phase(d);              // phase 2k+1: step k, loads of step k+3
       phase_end<63>();
@@ -499,7 +542,8 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
 // waves take the k-steps round-robin (wave w: steps w, w+8, ...).  Each wave
 // keeps D of its steps in flight in its own LDS ring: a slot holds the step's
 // A values (16 rows x 64 B, chunk-swizzled), the 16 rows' idx words (256 B)
-// and the B slice (KS rows x N).  All three arrive by direct-to-LDS loads,
+// and the B slice (KS rows x N; for B stored N x K, N rows of the step's 128
+// bytes with chunk c of row n at c ^ swzBT(n)).  All three arrive by direct-to-LDS loads,
 // issued through inline assembly and waited for with explicit vmcnt counts;
 // loads past the wave's last step read nothing, so every step issues the
 // same number of loads.  The 8 partial tiles are summed on chip in a fixed
@@ -536,7 +580,7 @@ __device__ __forceinline__ void wait_vm_upto15(int n) {
   }
 }
 
-template <int OP, int LAYOUT, int D>
+template <int OP, int LAYOUT, int D, int BL>
 __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const char* __restrict__ A_vals,
                                                                         const char* __restrict__ meta,
                                                                         const char* __restrict__ B, void* C, int M,
@@ -552,9 +596,10 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
   const int nw = nsteps > w ? (nsteps - w + kSmallWaves - 1) / kSmallWaves : 0;  // this wave's steps
   const int64_t rowA = (int64_t)K / 2 * ES, rowM = (int64_t)K / 8;
   const int64_t Mp = ((int64_t)M + 127) / 128 * 128;  // KBLOCK metadata rows per block
-  const int ldb = N * ES;                              // bytes per B row (multiple of 16)
+  const int ldb = N * ES;                              // bytes per K x N row (multiple of 16)
+  const int64_t ldbk = (int64_t)K * ES;                // bytes per N x K row
   const int chunks_per_row = ldb >> 4;
-  const int slice_instr = (KS * ldb) >> 10;            // 1 KiB per load (KS*ldb is a multiple of 1 KiB)
+  const int slice_instr = (KS * ldb) >> 10;            // 1 KiB per load (KS*ldb = 128*N is a multiple of 1 KiB)
   const int LPS = 2 + slice_instr;                     // loads per step
   const int64_t btotal = (int64_t)K * ldb;
   const int t16 = (m0 & 127) >> 4;                     // KBLOCK: row tile of the tile inside its 128-row group
@@ -565,7 +610,8 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
   // l = (row r = l/4, word g = l%4) -> the dword holding word g of row m0+r
   // (K-blocked: inside the tile's 128-row group, for row tile t16; row-major:
   // for 16-bit types the dword holding the u16 word g).  B: 1 KiB per load,
-  // lane l of load q -> chunk 64q + l of the slice.
+  // lane l of load q -> chunk 64q + l of the slice (N x K: row n = 8q + l/8,
+  // chunk (l%8) ^ swzBT(n) of the step).
   const int a_row = l >> 2, a_ch = (l & 3) ^ swzA(l >> 2);
   const int m_r = l >> 2, m_g = l & 3;
   const uint32_t offA = LAYOUT == SP24_LAYOUT_KBLOCK ? (uint32_t)(a_row * 64 + 16 * a_ch)
@@ -578,9 +624,14 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
   uint32_t offB[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const int c = q * 64 + l;
-    const int brow = c / chunks_per_row, bc = c - brow * chunks_per_row;
-    offB[q] = (uint32_t)(brow * ldb + 16 * bc);
+    if constexpr (BL == SP24_B_NK) {
+      const int n = 8 * q + (l >> 3);
+      offB[q] = (uint32_t)(n * ldbk + 16 * ((l & 7) ^ swzBT(n)));
+    } else {
+      const int c = q * 64 + l;
+      const int brow = c / chunks_per_row, bc = c - brow * chunks_per_row;
+      offB[q] = (uint32_t)(brow * ldb + 16 * bc);
+    }
   }
   const int nfull = K / KS;
   const i32x4 raRow = make_rsrc4(A_vals + (int64_t)m0 * rowA, (uint64_t)(M - m0) * rowA);
@@ -621,11 +672,27 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
     }
     dma16_asm(ra, la, oa, 0u);
     dma4_asm(rm, la + kSmallA, om, 0u);
-    const int64_t start = (int64_t)ks * KS * ldb;
-    const i32x4 rb = make_rsrc4(B + start, (in && start < btotal) ? (uint64_t)(btotal - start) : 0u);
+    if constexpr (BL == SP24_B_NK) {
+      // bytes ks*128 on of every row; the end of the row in the last step is
+      // masked per lane
+      const int64_t valid = ldbk - (int64_t)ks * 128;
+      const i32x4 rb = make_rsrc4(B + (int64_t)ks * 128, (in && valid > 0) ? (uint64_t)(N * ldbk - ks * 128) : 0u);
+      const bool tail = ks >= nfull && in;
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (q < slice_instr) dma16_asm(rb, la + kSmallA + kSmallM + q * 1024, offB[q], 0u);
+      for (int q = 0; q < 8; ++q) {
+        if (q < slice_instr) {
+          uint32_t ob = offB[q];
+          if (tail && 16 * ((l & 7) ^ swzBT(8 * q + (l >> 3))) >= valid) ob = kOOB;
+          dma16_asm(rb, la + kSmallA + kSmallM + q * 1024, ob, 0u);
+        }
+      }
+    } else {
+      const int64_t start = (int64_t)ks * KS * ldb;
+      const i32x4 rb = make_rsrc4(B + start, (in && start < btotal) ? (uint64_t)(btotal - start) : 0u);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q < slice_instr) dma16_asm(rb, la + kSmallA + kSmallM + q * 1024, offB[q], 0u);
+    }
   };
 
   i32x4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
@@ -641,6 +708,13 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn) {
       if (tn >= nt) break;
+      i32x8 b;
+      if constexpr (BL == SP24_B_NK) {
+        const int n = tn * 16 + s;
+        const i32x4 lo = *(const SP24_LDS i32x4*)(sb + n * 128 + 16 * (gb ^ swzBT(n)));
+        const i32x4 hi = *(const SP24_LDS i32x4*)(sb + n * 128 + 16 * ((gb + 4) ^ swzBT(n)));
+        b = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
       i32x2 p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -653,7 +727,8 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
           p[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SP24_LDS i32x2*)(sb + k * ldb + tn * 16 + (s & 1) * 8));
         }
       }
-      const i32x8 b = {p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+      b = i32x8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+      }
       // K-blocked 16-bit idx: the tile's word sits in half t16%2 of the dword
       if (LAYOUT == SP24_LAYOUT_KBLOCK && ES == 2 && (t16 & 1)) acc[tn] = smfmac16<OP, 1>(acc[tn], a, b, idx);
       else acc[tn] = smfmac16<OP, 0>(acc[tn], a, b, idx);
@@ -724,7 +799,7 @@ __global__ void scale_c_kernel(void* C, int64_t n, float beta) {
   }
 }
 
-template <int OP, int LAYOUT>
+template <int OP, int LAYOUT, int BL>
 static hipError_t launch_op(const void* A_vals, const uint32_t* meta, const void* B, void* C, int M, int N, int K,
                             float alpha, float beta, hipStream_t stream) {
   const char* a = static_cast<const char*>(A_vals);
@@ -739,37 +814,47 @@ static hipError_t launch_op(const void* A_vals, const uint32_t* meta, const void
   if (N <= 64) {
     const dim3 grid((unsigned)((M + 15) / 16)), block(kSmallWaves * 64);
     if ((int64_t)op_kstep(OP) * N * op_esize(OP) <= small_bslice<4>())
-      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 4>), grid, block, 0, stream, a, m, b, C, M, N, K, alpha, beta);
+      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 4, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, alpha,
+                         beta);
     else
-      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 2>), grid, block, 0, stream, a, m, b, C, M, N, K, alpha, beta);
+      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 2, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, alpha,
+                         beta);
     return hipGetLastError();
   }
   const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
-  hipLaunchKernelGGL((gemm_large8_kernel<OP, LAYOUT>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads8), 0,
+  hipLaunchKernelGGL((gemm_large8_kernel<OP, LAYOUT, BL>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads8), 0,
                      stream, a, m, b, C, M, N, K, alpha, beta, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 template <int OP>
-static hipError_t launch_layout(int layout, const void* A_vals, const uint32_t* meta, const void* B, void* C, int M,
-                                int N, int K, float alpha, float beta, hipStream_t stream) {
-  if (layout == SP24_LAYOUT_KBLOCK)
-    return launch_op<OP, SP24_LAYOUT_KBLOCK>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
-  return launch_op<OP, SP24_LAYOUT_ROW>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+static hipError_t launch_layout(int layout, int b_layout, const void* A_vals, const uint32_t* meta, const void* B,
+                                void* C, int M, int N, int K, float alpha, float beta, hipStream_t stream) {
+  if (layout == SP24_LAYOUT_KBLOCK) {
+    if (b_layout == SP24_B_NK)
+      return launch_op<OP, SP24_LAYOUT_KBLOCK, SP24_B_NK>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+    return launch_op<OP, SP24_LAYOUT_KBLOCK, SP24_B_KN>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+  }
+  if (b_layout == SP24_B_NK)
+    return launch_op<OP, SP24_LAYOUT_ROW, SP24_B_NK>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+  return launch_op<OP, SP24_LAYOUT_ROW, SP24_B_KN>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
 }
 
-hipError_t launch_gemm(int op, int layout, const void* A_vals, const uint32_t* meta, const void* B, void* C, int M,
-                       int N, int K, float alpha, float beta, hipStream_t stream) {
+hipError_t launch_gemm(int op, int layout, int b_layout, const void* A_vals, const uint32_t* meta, const void* B,
+                       void* C, int M, int N, int K, float alpha, float beta, hipStream_t stream) {
+#define SP24_CASE(O) \
+  case O: return launch_layout<O>(layout, b_layout, A_vals, meta, B, C, M, N, K, alpha, beta, stream);
   switch (op) {
-    case OP_F16: return launch_layout<OP_F16>(layout, A_vals, meta, B, C, M, N, K, alpha, beta, stream);
-    case OP_BF16: return launch_layout<OP_BF16>(layout, A_vals, meta, B, C, M, N, K, alpha, beta, stream);
-    case OP_I8: return launch_layout<OP_I8>(layout, A_vals, meta, B, C, M, N, K, alpha, beta, stream);
-    case OP_FP8_FP8: return launch_layout<OP_FP8_FP8>(layout, A_vals, meta, B, C, M, N, K, alpha, beta, stream);
-    case OP_FP8_BF8: return launch_layout<OP_FP8_BF8>(layout, A_vals, meta, B, C, M, N, K, alpha, beta, stream);
-    case OP_BF8_FP8: return launch_layout<OP_BF8_FP8>(layout, A_vals, meta, B, C, M, N, K, alpha, beta, stream);
-    case OP_BF8_BF8: return launch_layout<OP_BF8_BF8>(layout, A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+    SP24_CASE(OP_F16)
+    SP24_CASE(OP_BF16)
+    SP24_CASE(OP_I8)
+    SP24_CASE(OP_FP8_FP8)
+    SP24_CASE(OP_FP8_BF8)
+    SP24_CASE(OP_BF8_FP8)
+    SP24_CASE(OP_BF8_BF8)
     default: return hipErrorInvalidValue;
   }
+#undef SP24_CASE
 }
 
 }  // namespace sp24

@@ -93,8 +93,8 @@ def test_gemm_argument_errors(L):
     F16, I8, E4, E5, BF = L.SP24_F16, L.SP24_I8, L.SP24_FP8_E4M3, L.SP24_BF8_E5M2, L.SP24_BF16
     A, Mt, B, C = P, 2 * P, 3 * P, 8 * P
     for lay in (L.SP24_LAYOUT_ROW, L.SP24_LAYOUT_KBLOCK):
-        def g(a, m, at, b, bt, c, *rest):
-            return L.sp24_gemm(a, m, at, lay, b, bt, c, *rest)
+        def g(a, m, at, b, bt, c, *rest, bl=L.SP24_B_KN):
+            return L.sp24_gemm(a, m, at, lay, b, bt, bl, c, *rest)
         assert g(A, Mt, F16, B, BF, C, 64, 64, 64, 1.0, 0.0, None, 0, None) == 2   # mixed 16-bit pair
         assert g(A, Mt, F16, B, E4, C, 64, 64, 64, 1.0, 0.0, None, 0, None) == 2
         assert g(A, Mt, I8, B, F16, C, 64, 64, 64, 1.0, 0.0, None, 0, None) == 2
@@ -110,13 +110,19 @@ def test_gemm_argument_errors(L):
         assert g(A, Mt, F16, B, F16, C, 64, 0, 64, 1.0, 0.0, None, 0, None) == 0        # N == 0
         assert g(A, Mt, F16, B, F16, C, -4, 64, 64, 1.0, 0.0, None, 0, None) == 1
         assert g(A, Mt, F16, B, F16, C, 64, 1 << 23, 64, 1.0, 0.0, None, 0, None) == 2  # 128 rows of B > 2 GiB
+        assert g(A, Mt, F16, B, F16, C, 64, 64, 64, 1.0, 0.0, None, 0, None, bl=2) == 2  # unknown B layout
+        assert g(A, Mt, F16, B, F16, B + 64, 64, 64, 64, 1.0, 0.0, None, 0, None, bl=L.SP24_B_NK) == 1
+        # B stored N x K: 256 of its rows are addressed with 32-bit offsets, so K is bounded
+        assert g(A, Mt, F16, B, F16, C, 0, 64, 1 << 22, 1.0, 0.0, None, 0, None, bl=L.SP24_B_NK) == 2
+        assert g(A, Mt, F16, B, F16, C, 0, 64, 1 << 22, 1.0, 0.0, None, 0, None) == 0
         # every documented pair passes validation up to the launch (checked with M == 0)
         for a, b in [(F16, F16), (BF, BF), (I8, I8), (E4, E4), (E4, E5), (E5, E4), (E5, E5)]:
-            assert g(A, Mt, a, B, b, C, 0, 64, 64, 1.0, 0.0, None, 0, None) == 0
-    assert L.sp24_gemm(A, Mt, F16, 5, B, F16, C, 64, 64, 64, 1.0, 0.0, None, 0, None) == 2   # unknown layout
+            for bl in (L.SP24_B_KN, L.SP24_B_NK):
+                assert g(A, Mt, a, B, b, C, 0, 64, 64, 1.0, 0.0, None, 0, None, bl=bl) == 0
+    assert L.sp24_gemm(A, Mt, F16, 5, B, F16, 0, C, 64, 64, 64, 1.0, 0.0, None, 0, None) == 2   # unknown layout
     # the row-major layout addresses a 256-row tile with 32-bit offsets: K is bounded
     big_k = 1 << 23
-    assert L.sp24_gemm(A, Mt, F16, L.SP24_LAYOUT_ROW, B, F16, C, 64, 64, big_k, 1.0, 0.0, None, 0, None) == 2
+    assert L.sp24_gemm(A, Mt, F16, L.SP24_LAYOUT_ROW, B, F16, 0, C, 64, 64, big_k, 1.0, 0.0, None, 0, None) == 2
 
 
 def test_decompress_and_validate_argument_errors(L):

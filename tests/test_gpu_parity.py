@@ -42,6 +42,7 @@ def pkg():
 DEV = "cuda:0"
 ROW, KBLOCK = 0, 1
 LAYOUTS = [ROW, KBLOCK]
+KN, NK = 0, 1  # B stored K x N, or transposed (N x K)
 TVIEW = {wl.F16: torch.int16, wl.BF16: torch.int16, wl.I8: torch.int8, wl.E4M3: torch.uint8, wl.E5M2: torch.uint8}
 TTYPE = {wl.F16: torch.float16, wl.BF16: torch.bfloat16, wl.I8: torch.int8, wl.E4M3: torch.float8_e4m3fn,
          wl.E5M2: torch.float8_e5m2}
@@ -81,20 +82,26 @@ def check_compress(pkg, A_bits, dtype, layout=KBLOCK):
     return ov, om
 
 
-def run_gemm(pkg, vals_bits, meta_words, a_type, B_bits, b_type, C=None, alpha=1.0, beta=0.0, layout=KBLOCK):
+def b_on_dev(B_bits, b_type, b_layout):
+    """K x N device view of B: contiguous, or the transpose of a contiguous N x K copy."""
+    return to_dev(B_bits, b_type) if b_layout == KN else to_dev(np.ascontiguousarray(B_bits.T), b_type).t()
+
+
+def run_gemm(pkg, vals_bits, meta_words, a_type, B_bits, b_type, C=None, alpha=1.0, beta=0.0, layout=KBLOCK,
+             b_layout=KN):
     vals_bits, meta_words = in_layout(vals_bits, meta_words, a_type, layout)
     V = to_dev(vals_bits, a_type)
     Mt = torch.from_numpy(np.ascontiguousarray(meta_words).view(np.int32)).to(DEV)
-    B = to_dev(B_bits, b_type)
+    B = b_on_dev(B_bits, b_type, b_layout)
     Ct = None if C is None else torch.from_numpy(np.ascontiguousarray(C)).to(DEV)
     D = pkg.gemm(V, Mt, B, Ct, alpha=alpha, beta=beta, a_type=a_type, b_type=b_type, layout=layout)
     torch.cuda.synchronize()
     return D
 
 
-def check_gemm_full(pkg, vals, meta, a_type, B, b_type, C=None, alpha=1.0, beta=0.0, layout=KBLOCK):
+def check_gemm_full(pkg, vals, meta, a_type, B, b_type, C=None, alpha=1.0, beta=0.0, layout=KBLOCK, b_layout=KN):
     """vals / meta: the oracle's row-major compressed A (moved into `layout` for the GPU)."""
-    D = run_gemm(pkg, vals, meta, a_type, B, b_type, C, alpha, beta, layout).cpu().numpy()
+    D = run_gemm(pkg, vals, meta, a_type, B, b_type, C, alpha, beta, layout, b_layout).cpu().numpy()
     if a_type == wl.I8:
         ref = oracle.gemm_i64(vals, meta, B, C, beta_one=(beta == 1.0))
         assert np.array_equal(D.astype(np.int64), ref)
@@ -181,6 +188,35 @@ def test_gemm_random(pkg, a_type, b_type, M, N, K, layout):
     check_gemm_full(pkg, vals, meta, a_type, c.B, b_type, layout=layout)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("a_type,b_type", PAIRS)
+@pytest.mark.parametrize("M,N,K", [(300, 272, 160), (512, 512, 544), (17, 96, 256), (96, 48, 352),
+                                   (40, 16, 128), (600, 64, 1024), (1, 128, 64), (257, 8, 4128)])
+def test_gemm_random_b_transposed(pkg, a_type, b_type, M, N, K, layout):
+    """B stored N x K (K contiguous)."""
+    if (N * wl.ESIZE[b_type]) % 16:
+        pytest.skip("leading dimension not supported")
+    _say(f"gemm B^T a={a_type} b={b_type} M={M} N={N} K={K} layout={layout}")
+    c = wl.random_case(23, M, N, K, a_type, b_type)
+    vals, meta = oracle.prune_compress(c.A, a_type)
+    check_gemm_full(pkg, vals, meta, a_type, c.B, b_type, layout=layout, b_layout=NK)
+
+
+@pytest.mark.parametrize("a_type,b_type", [(wl.F16, wl.F16), (wl.I8, wl.I8), (wl.E5M2, wl.E4M3)])
+@pytest.mark.parametrize("N", [16, 48, 512])
+def test_b_layouts_give_identical_bits(pkg, a_type, b_type, N):
+    """Both B layouts deliver the same fragments to the same instruction
+    sequence: outputs agree bit for bit (K with a ragged last step)."""
+    _say(f"B layouts agree a={a_type} N={N}")
+    c = wl.random_case(37, 520, N, 736 if wl.ESIZE[a_type] == 2 else 800, a_type, b_type)
+    A = to_dev(c.A, a_type)
+    V, Mt = pkg.prune_compress(A, a_type, KBLOCK)
+    D1 = pkg.gemm(V, Mt, b_on_dev(c.B, b_type, KN), a_type=a_type, b_type=b_type)
+    D2 = pkg.gemm(V, Mt, b_on_dev(c.B, b_type, NK), a_type=a_type, b_type=b_type)
+    torch.cuda.synchronize()
+    assert torch.equal(D1.view(torch.int32), D2.view(torch.int32))
+
+
 @pytest.mark.parametrize("a_type,b_type", [(wl.F16, wl.F16), (wl.I8, wl.I8), (wl.E5M2, wl.E4M3)])
 @pytest.mark.parametrize("N", [32, 512])
 def test_layouts_give_identical_bits(pkg, a_type, b_type, N):
@@ -199,20 +235,22 @@ def test_layouts_give_identical_bits(pkg, a_type, b_type, N):
 
 @pytest.mark.parametrize("a_type,b_type", [(wl.F16, wl.F16), (wl.BF16, wl.BF16), (wl.E4M3, wl.E5M2)])
 @pytest.mark.parametrize("N", [32, 320])
-def test_gemm_alpha_beta(pkg, a_type, b_type, N):
-    _say(f"gemm alpha/beta a={a_type} N={N}")
+@pytest.mark.parametrize("b_layout", [KN, NK])
+def test_gemm_alpha_beta(pkg, a_type, b_type, N, b_layout):
+    _say(f"gemm alpha/beta a={a_type} N={N} b_layout={b_layout}")
     c = wl.random_case(5, 130, N, 192, a_type, b_type, beta=1.0)
     vals, meta = oracle.prune_compress(c.A, a_type)
-    check_gemm_full(pkg, vals, meta, a_type, c.B, b_type, c.C, alpha=-0.5, beta=1.5)
-    check_gemm_full(pkg, vals, meta, a_type, c.B, b_type, c.C, alpha=0.0, beta=2.0)
+    check_gemm_full(pkg, vals, meta, a_type, c.B, b_type, c.C, alpha=-0.5, beta=1.5, b_layout=b_layout)
+    check_gemm_full(pkg, vals, meta, a_type, c.B, b_type, c.C, alpha=0.0, beta=2.0, b_layout=b_layout)
 
 
 @pytest.mark.parametrize("N", [32, 272])
-def test_gemm_int8_beta_one(pkg, N):
-    _say(f"gemm int8 beta=1 N={N}")
+@pytest.mark.parametrize("b_layout", [KN, NK])
+def test_gemm_int8_beta_one(pkg, N, b_layout):
+    _say(f"gemm int8 beta=1 N={N} b_layout={b_layout}")
     c = wl.random_case(6, 77, N, 256, wl.I8, wl.I8, beta=1.0)
     vals, meta = oracle.prune_compress(c.A, wl.I8)
-    check_gemm_full(pkg, vals, meta, wl.I8, c.B, wl.I8, c.C, beta=1.0)
+    check_gemm_full(pkg, vals, meta, wl.I8, c.B, wl.I8, c.C, beta=1.0, b_layout=b_layout)
 
 
 @pytest.mark.parametrize("N", [48, 512])
@@ -269,9 +307,11 @@ def test_gemm_gpu_compressed_input(pkg):
 
 # ---- the named workloads at their full sizes -----------------------------------
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["tiny_f16", "f16_4096", "bf16_linear_n16", "bf16_linear_n4096", "i8_8192",
-                                  "fp8_bf8_8192x16384", "bf8_bf8_8192x16384", "f16_8192"])
-def test_workload_full_size(pkg, name):
+@pytest.mark.parametrize("name,b_layout", [("tiny_f16", KN), ("f16_4096", KN), ("bf16_linear_n16", KN),
+                                           ("bf16_linear_n4096", KN), ("i8_8192", KN), ("fp8_bf8_8192x16384", KN),
+                                           ("bf8_bf8_8192x16384", KN), ("f16_8192", KN),
+                                           ("bf16_linear_n16", NK), ("bf16_linear_n4096", NK), ("f16_8192", NK)])
+def test_workload_full_size(pkg, name, b_layout):
     _say(f"workload {name}: generating inputs")
     w = wl.make(name)
     _say(f"workload {name}: M={w.M} N={w.N} K={w.K} compress")
@@ -290,13 +330,13 @@ def test_workload_full_size(pkg, name):
         pairs = np.array([(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)])
         assert np.array_equal(codes[:, 0::2], pairs[w.notes["pattern_pick"], 0])
     del A
-    _say(f"workload {name}: gemm")
-    B = to_dev(w.B, w.b_type)
+    _say(f"workload {name}: gemm (b_layout={b_layout})")
+    B = b_on_dev(w.B, w.b_type, b_layout)
     C = None if w.C is None else torch.from_numpy(w.C).to(DEV)
     D = pkg.gemm(vals_d, meta_d, B, C, alpha=w.alpha, beta=w.beta, a_type=w.a_type, b_type=w.b_type)
     torch.cuda.synchronize()
     if w.M * w.N <= 64 * 64:
-        check_gemm_full(pkg, ov, om, w.a_type, w.B, w.b_type, w.C, w.alpha, w.beta)
+        check_gemm_full(pkg, ov, om, w.a_type, w.B, w.b_type, w.C, w.alpha, w.beta, b_layout=b_layout)
     else:
         check_gemm_sampled(D, ov, om, w)
 
