@@ -119,21 +119,30 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kernel(const 
   }
 }
 
-// K-blocked layout.  Workgroup (row tile rt, block b) covers rows
-// rt*128 .. +128 of block b; thread t handles chunk t%8 of rows
-// rt*128 + t/8 + 32u (u < 4).  Consecutive workgroups take consecutive
-// blocks of the same row tile, so the workgroups in flight read one
-// contiguous band of A (DRAM-page friendly) while each writes one 8 KiB run
-// of values.  Chunks past K (the tail of a partial last block) are written
-// as zero values with zero codes, and rows past M up to the 128-row group
-// boundary get zero codes (the metadata is padded to whole groups).
+// K-blocked layout.  Workgroup (row tile rt, block group) covers rows
+// rt*128 .. +128 of NB consecutive blocks; thread t handles chunk t % (8*NB)
+// of rows rt*128 + t/(8*NB) + (256/(8*NB))*u.  Consecutive workgroups take
+// consecutive block groups of the same row tile, so the workgroups in
+// flight read one contiguous band of A (DRAM-page friendly); each writes
+// one 8 KiB run of values per block.  Chunks past K (the tail of a partial
+// last block) are written as zero values with zero codes, and rows past M
+// up to the 128-row group boundary get zero codes (the metadata is padded
+// to whole groups).
 //
 // A chunk's codes are half of a code word: chunk c of a row
 // holds half c%2 of the row's word g = c/2 (bytes for 16-bit types, 16-bit
 // halves for 8-bit types).  In the 128-row group, word g of row 16t + r sits
 // at u16 index ((r*4 + g)*4 + t/2)*2 + t%2 (16-bit types) or u32 index
-// (r*4 + g)*8 + t (8-bit types).
+// (r*4 + g)*8 + t (8-bit types).  That interleaving scatters a thread's
+// codes, so they are collected in LDS and each block's group of codes
+// (1 or 2 KiB, contiguous) is written with 16-byte stores.
 constexpr int kKbRowsPerTile = 128;
+
+// Blocks per workgroup: 16-bit types take 4 (each row's 512 contiguous bytes
+// are read by 32 lanes), 8-bit types 1 (their metadata is twice as large and
+// the staging writes collide in LDS with more blocks).
+template <int ES>
+__host__ __device__ constexpr int kb_blocks_per_wg() { return ES == 2 ? 4 : 1; }
 
 template <int ES, bool INT>
 __global__ __launch_bounds__(kCompressThreads) void prune_compress_kblock_kernel(const char* __restrict__ A,
@@ -141,54 +150,54 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kblock_kernel
                                                                                    char* __restrict__ meta,
                                                                                    int64_t M, int64_t K,
                                                                                    uint32_t nblk) {
+  constexpr int NB = kb_blocks_per_wg<ES>();
   constexpr int MB = ES == 2 ? 8 : 16;         // metadata bytes per row per block
   constexpr int CE = 16 / ES;                   // dense elements per chunk
-  const int64_t b = blockIdx.x % nblk;
-  const uint32_t rt = blockIdx.x / nblk;
+  constexpr int GB = 128 * MB;                  // metadata bytes of one 128-row group per block
+  constexpr int CPR = 8 * NB;                   // chunks per row in the tile
+  constexpr int RPR = kCompressThreads / CPR;   // rows per load round
+  constexpr int NR = 128 / RPR;                 // load rounds
+  __shared__ __attribute__((aligned(16))) char lmeta[NB * GB];
+  const uint32_t nwb = (nblk + NB - 1) / NB;
+  const int64_t b0 = (int64_t)(blockIdx.x % nwb) * NB;
+  const uint32_t rt = blockIdx.x / nwb;
   const int64_t Mp = (M + 127) / 128 * 128;
-  const int c = threadIdx.x & 7;
-  const int64_t kcol = b * (8 * CE) + (int64_t)c * CE;  // first dense column of the chunk
+  const int cc = threadIdx.x % CPR;             // chunk in the tile row
+  const int bi = cc / 8, c = cc % 8;            // block in the tile, chunk in the block
+  const int64_t b = b0 + bi;
+  const int64_t kcol = b * (8 * CE) + (int64_t)c * CE;
   const bool inside = kcol < K;
   const int64_t rowbytes = K * ES;
-  i32x4 in[kCompressUnroll];
+  i32x4 in[NR];
 #pragma unroll
-  for (int u = 0; u < kCompressUnroll; ++u) {
-    const int64_t row = (int64_t)rt * kKbRowsPerTile + (threadIdx.x >> 3) + 32 * u;
+  for (int u = 0; u < NR; ++u) {
+    const int64_t row = (int64_t)rt * kKbRowsPerTile + threadIdx.x / CPR + RPR * u;
     in[u] = i32x4{0, 0, 0, 0};
     if (row < M && inside)
       in[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(A + row * rowbytes + kcol * ES));
   }
+  char* lm = lmeta + bi * GB;
 #pragma unroll
-  for (int u = 0; u < kCompressUnroll; ++u) {
-    const int rr = (threadIdx.x >> 3) + 32 * u;  // row inside the 128-row group
+  for (int u = 0; u < NR; ++u) {
+    const int rr = threadIdx.x / CPR + RPR * u;  // row inside the 128-row group
     const int64_t row = (int64_t)rt * kKbRowsPerTile + rr;
     const int t = rr >> 4, r = rr & 15;
-    char* mgroup = meta + (b * Mp + (int64_t)rt * 128) * MB;
-    if (row >= M) {  // padding rows of the last group: zero codes
-      if constexpr (ES == 2)
-        __builtin_nontemporal_store((uint8_t)0, reinterpret_cast<uint8_t*>(mgroup + (((r * 4 + c / 2) * 4 + t / 2) * 2 + (t & 1)) * 2 + (c & 1)));
-      else
-        __builtin_nontemporal_store((uint16_t)0, reinterpret_cast<uint16_t*>(mgroup + ((r * 4 + c / 2) * 8 + t) * 4 + (c & 1) * 2));
-      continue;
-    }
-    const int64_t slot = b * M + row;
     const uint32_t d0 = (uint32_t)in[u][0], d1 = (uint32_t)in[u][1];
     const uint32_t d2 = (uint32_t)in[u][2], d3 = (uint32_t)in[u][3];
     i32x2 out = {0, 0};
-    i32x2* vp = reinterpret_cast<i32x2*>(vals + slot * 64 + c * 8);
+    const bool live = row < M && inside;  // padding rows and chunks past K: zero codes
     if constexpr (ES == 2) {
       uint8_t code = 0;
-      if (inside) {
+      if (live) {
         uint32_t n0, n1;
         out[0] = (int)group16((uint64_t)d0 | ((uint64_t)d1 << 32), n0);
         out[1] = (int)group16((uint64_t)d2 | ((uint64_t)d3 << 32), n1);
         code = (uint8_t)(n0 | (n1 << 4));
       }
-      __builtin_nontemporal_store(out, vp);
-      __builtin_nontemporal_store(code, reinterpret_cast<uint8_t*>(mgroup + (((r * 4 + c / 2) * 4 + t / 2) * 2 + (t & 1)) * 2 + (c & 1)));
+      lm[(((r * 4 + c / 2) * 4 + t / 2) * 2 + (t & 1)) * 2 + (c & 1)] = (char)code;
     } else {
       uint16_t code = 0;
-      if (inside) {
+      if (live) {
         uint32_t n0, n1, n2, n3;
         const uint32_t v0 = group8<INT>(d0, n0), v1 = group8<INT>(d1, n1);
         const uint32_t v2 = group8<INT>(d2, n2), v3 = group8<INT>(d3, n3);
@@ -196,9 +205,19 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kblock_kernel
         out[1] = (int)(v2 | (v3 << 16));
         code = (uint16_t)(n0 | (n1 << 4) | (n2 << 8) | (n3 << 12));
       }
-      __builtin_nontemporal_store(out, vp);
-      __builtin_nontemporal_store(code, reinterpret_cast<uint16_t*>(mgroup + ((r * 4 + c / 2) * 8 + t) * 4 + (c & 1) * 2));
+      *reinterpret_cast<uint16_t*>(lm + ((r * 4 + c / 2) * 8 + t) * 4 + (c & 1) * 2) = code;
     }
+    if (row < M && b < (int64_t)nblk)
+      __builtin_nontemporal_store(out, reinterpret_cast<i32x2*>(vals + (b * M + row) * 64 + c * 8));
+  }
+  __syncthreads();
+  // each block's group metadata, 16 bytes per thread
+#pragma unroll
+  for (int q = threadIdx.x; q < NB * GB / 16; q += kCompressThreads) {
+    const int bq = q / (GB / 16), w = q % (GB / 16);
+    if (b0 + bq < (int64_t)nblk)
+      __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(lmeta + 16 * q),
+                                  reinterpret_cast<i32x4*>(meta + ((b0 + bq) * Mp + (int64_t)rt * 128) * MB) + w);
   }
 }
 
@@ -213,8 +232,10 @@ hipError_t launch_prune_compress(const void* A, void* vals, uint32_t* meta, int6
     const int64_t kb = es == 2 ? 64 : 128;
     const int64_t nblk = (K + kb - 1) / kb;
     const int64_t row_tiles = (M + kKbRowsPerTile - 1) / kKbRowsPerTile;
-    if (row_tiles * nblk > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(row_tiles * nblk));
+    const int64_t nwb = (nblk + (es == 2 ? kb_blocks_per_wg<2>() : kb_blocks_per_wg<1>()) - 1) /
+                        (es == 2 ? kb_blocks_per_wg<2>() : kb_blocks_per_wg<1>());
+    if (row_tiles * nwb > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(row_tiles * nwb));
     const char* a = static_cast<const char*>(A);
     char* v = static_cast<char*>(vals);
     char* m = reinterpret_cast<char*>(meta);
