@@ -84,8 +84,12 @@ constexpr int kLdsB = 32768;                      // KS * BN * esize = 32 KiB fo
 constexpr int kLdsM = kBM * 16;                   // 4 KiB (16-bit inputs use half)
 constexpr int kLdsStage = kLdsA + kLdsB + kLdsM;  // 52 KiB; three stages = 156 KiB
 
-// A tile: row r, 16-byte chunk c stored at chunk c ^ swzA(r) (conflict-free
-// for 16 lanes reading 16 consecutive rows at one chunk).
+// A tile of the large kernel: fragment order.  Row tile t (16 rows) fills
+// bytes 1024t .. +1024, and the 16 bytes fragment lane l needs (row l%16,
+// chunk l/16) sit at 16l, so each fragment is one contiguous read.  (Stored
+// row-major with an XOR swizzle, the same reads measured about 60% of the
+// LDS read rate of contiguous ones on gfx950.)  The small-N kernel stores its
+// A rows row-major with chunk c of row r at chunk c ^ swzA(r).
 __device__ __forceinline__ int swzA(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
 // B tile, 16-bit: row k holds 256 columns = 16 pairs of chunks; pair p stored
 // at p ^ swzB16(k).  8-bit: 16 chunks per row; chunk c stored at c ^ swzB8(k).
@@ -122,8 +126,8 @@ __device__ __forceinline__ LaneConsts8 make_lane_consts8(int w, int l, int64_t r
   LaneConsts8 c;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int row = (w * 2 + i) * 16 + (l >> 2);
-    c.voA[i] = (uint32_t)(row * (KB ? 64 : rowA) + 16 * ((l & 3) ^ swzA(row)));
+    const int row = (w * 2 + i) * 16 + (l & 15);  // lane l -> row l%16, chunk l/16
+    c.voA[i] = (uint32_t)(row * (KB ? 64 : rowA) + 16 * (l >> 4));
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -154,7 +158,7 @@ __device__ __forceinline__ LaneConsts8 make_lane_consts8(int w, int l, int64_t r
     }
   }
   const int wm = w >> 2, wn = w & 3, ga = l >> 4, r16 = l & 15;
-  c.ldsA = (wm * 128 + r16) * 64 + 16 * (ga ^ swzA(r16));
+  c.ldsA = wm * 8 * 1024 + 16 * l;  // fragment order: one contiguous 1 KiB read per row tile
   if constexpr (KB)  // this lane's 8 words of its 128-row group, contiguous
     c.ldsM = kLdsA + kLdsB + wm * 128 * MB + (r16 * 4 + ga) * (ES == 2 ? 16 : 32);
   else               // [row][MB]
@@ -268,9 +272,7 @@ __device__ __forceinline__ void dma_piece(const DmaStep& d, const LaneConsts8& l
   if constexpr (P < 2) {
     uint32_t off = lc.voA[P] + d.offA;
     if (d.tail) {
-      const int l = lane_id();
-      const int row = (w * 2 + P) * 16 + (l >> 2);
-      if (16 * ((l & 3) ^ swzA(row)) >= d.validA) off = kOOB;
+      if (16 * (lane_id() >> 4) >= d.validA) off = kOOB;
     }
     dma16_asm(d.rA, d.lds + (w * 2 + P) * 1024, off, 0u);
   } else if constexpr (P < 6) {
