@@ -279,8 +279,9 @@ def main():
     if not args.no_cpu:
         rows = args.cpu_rows
         if rows is None:
-            # the oracle does ~0.6e9 multiply-adds per second per core: ~1.6e11 of them is 10-30 s on 16 cores
-            rows = max(1, min(w.M, int(1.6e11 / max(1, w.N * w.K // 2))))
+            # the oracle does ~2e9 multiply-adds per second per core on the GPU machine's
+            # host (measured): ~4.8e11 of them is ~15 s on 16 cores (capped at all M rows)
+            rows = max(1, min(w.M, int(4.8e11 / max(1, w.N * w.K // 2))))
         res["cpu_baseline"] = cpu_baseline(w, rows)
     print(json.dumps(res), flush=True)
 
