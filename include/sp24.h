@@ -82,7 +82,9 @@ typedef enum {
   SP24_BF16 = 2,
   SP24_I8 = 3,
   SP24_FP8_E4M3 = 4,
-  SP24_BF8_E5M2 = 5
+  SP24_BF8_E5M2 = 5,
+  SP24_F32 = 6, /* output (C / D) type only */
+  SP24_I32 = 7  /* output (C / D) type only */
 } sp24_dtype;
 
 typedef enum {
@@ -178,6 +180,34 @@ int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, 
 int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, const void* B, int b_type,
               int b_layout, void* C, int64_t M, int64_t N, int64_t K, float alpha, float beta, void* workspace,
               size_t workspace_bytes, void* stream);
+
+/*
+ * sp24_gemm_ex -- sp24_gemm with a choice of output type and a bias:
+ *   D[i][j] = round_c_type(alpha * (expand(A_vals, meta) * B)[i][j]
+ *                          + beta * C[i][j] + bias[j]),
+ * D written over C.  The product accumulates in fp32 (exact int32 for int8)
+ * exactly as in sp24_gemm; the sum with beta*C and the bias is formed in
+ * fp32 and rounded once, to nearest even, into c_type.  (The pages' RDNA4
+ * builtins accumulate into FP16 or BF16 directly ("RDNA4 sparse WMMA
+ * builtins", sections "FP16-accumulate builtins" and "BF16-accumulate
+ * builtins"); the CDNA sparse instructions accumulate in FP32 only, so a
+ * 16-bit result is produced here by one rounding at the end.  The bias is
+ * the linear-layer epilogue this library adds.)
+ *
+ *   c_type   SP24_F32, SP24_F16 or SP24_BF16 for floating inputs;
+ *            SP24_I32 for int8 x int8.  C and D are M x N elements of c_type.
+ *            C (when beta != 0) is read in c_type and widened to fp32.
+ *   bias     NULL, or N float32 values (device pointer, 16-byte aligned)
+ *            added to every row.  Floating inputs only.
+ *   Everything else as for sp24_gemm; sp24_gemm(...) is sp24_gemm_ex with
+ *   c_type = SP24_F32 (SP24_I32 for int8) and bias = NULL.
+ * Errors: as sp24_gemm, plus UNSUPPORTED (c_type not allowed for the input
+ * types, a bias with int8 inputs), MISALIGNED (bias), INVALID_VALUE (C
+ * overlapping the bias).
+ */
+int sp24_gemm_ex(const void* A_vals, const uint32_t* meta, int a_type, int layout, const void* B, int b_type,
+                 int b_layout, void* C, int c_type, const float* bias, int64_t M, int64_t N, int64_t K, float alpha,
+                 float beta, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * sp24_decompress -- (A_vals, meta) -> dense A, the inverse of compression:

@@ -59,7 +59,9 @@ def _load():
         lib.orc_decompress.argtypes = [P, P, P, I64, I64, I]
         lib.orc_count_invalid.argtypes = [P, I64, I64]
         lib.orc_count_invalid.restype = I64
-        lib.orc_gemm_f64.argtypes = [P, P, I, P, I, P, P, P, I64, I64, I64, D, D]
+        lib.orc_gemm_f64.argtypes = [P, P, I, P, I, P, P, P, P, I64, I64, I64, D, D]
+        lib.orc_round_to.argtypes = [D, I]
+        lib.orc_round_to.restype = ctypes.c_uint32
         lib.orc_gemm_i64.argtypes = [P, P, P, P, P, I64, I64, I64, I]
         lib.orc_gemm_points_f64.argtypes = [P, P, I, P, I, P, I64, I64, I64, D, D, I64, P, P, P, P]
         lib.orc_gemm_points_i64.argtypes = [P, P, P, P, I64, I64, I64, I, I64, P, P, P]
@@ -141,11 +143,23 @@ def count_invalid(meta, K):
     return int(n)
 
 
-def gemm_f64(vals, meta, a_type, B, b_type, C=None, alpha=1.0, beta=0.0, want_abs=True):
-    """alpha * expand(vals, meta) @ B + beta * C in float64 (float types).
+def round_to(x, dtype) -> np.ndarray:
+    """Bit patterns (uint16) of the nearest fp16 / bf16 values to the float64
+    array x, ties to even (C oracle, one element at a time)."""
+    lib = _load()
+    if dtype not in (F16, BF16):
+        raise ValueError("round_to: fp16 or bf16 only")
+    flat = np.ascontiguousarray(x, dtype=np.float64).reshape(-1)
+    out = np.array([lib.orc_round_to(float(v), dtype) for v in flat], dtype=np.uint16)
+    return out.reshape(np.shape(x))
 
-    Returns (D, S) where S = |alpha| * sum|a*b| + |beta*C| per element (None
-    if want_abs is False)."""
+
+def gemm_f64(vals, meta, a_type, B, b_type, C=None, alpha=1.0, beta=0.0, want_abs=True, bias=None):
+    """alpha * expand(vals, meta) @ B + beta * C + bias in float64 (float types).
+
+    C is given as float32 values (a 16-bit C widened, which is exact); bias is
+    None or N float32 values.  Returns (D, S) where S = |alpha| * sum|a*b| +
+    |beta*C| + |bias| per element (None if want_abs is False)."""
     lib = _load()
     vals = _as_bits(vals, a_type)
     B = _as_bits(B, b_type)
@@ -160,9 +174,13 @@ def gemm_f64(vals, meta, a_type, B, b_type, C=None, alpha=1.0, beta=0.0, want_ab
             raise ValueError("C shape")
     else:
         C = None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        if bias.shape != (N,):
+            raise ValueError("bias shape")
     D = np.empty((M, N), dtype=np.float64)
     S = np.empty((M, N), dtype=np.float64) if want_abs else None
-    _check(lib.orc_gemm_f64(_ptr(vals), _ptr(meta), a_type, _ptr(B), b_type, _ptr(C), _ptr(D), _ptr(S),
+    _check(lib.orc_gemm_f64(_ptr(vals), _ptr(meta), a_type, _ptr(B), b_type, _ptr(C), _ptr(bias), _ptr(D), _ptr(S),
                             M, N, K, float(alpha), float(beta)), "gemm_f64")
     return D, S
 

@@ -20,6 +20,12 @@
  *     index aligns each compressed A value with its row of B (section
  *     "Structured sparsity"; the ISA page for v_smfmac_f32_32x32x32_bf8_bf8,
  *     section "Semantics": D = A(sparse) * B + D).
+ *   - Output rounding (the library's 16-bit output option): the exact fp64
+ *     result is rounded once to the nearest fp16 / bf16 value, ties to even.
+ *     The pages' RDNA4 builtins accumulate into FP16 / BF16 ("RDNA4 sparse
+ *     WMMA builtins", sections "FP16-accumulate builtins" and
+ *     "BF16-accumulate builtins"); the CDNA sparse instructions accumulate in
+ *     FP32 only, so the library rounds the fp32 result at the end instead.
  *   - The pruning rule (keep the two largest magnitudes, ties to the lower
  *     position) is not fixed by the pages, which only say weights are pruned
  *     offline ("RDNA4 sparse WMMA builtins", section "Instruction
@@ -95,6 +101,43 @@ double orc_decode(uint32_t bits, int dtype) {
 /* Magnitude key used to rank the 4 elements of a group.  For the float
  * formats the bit pattern with the sign cleared is monotone in |x| (NaN sorts
  * above Inf, -0 equals +0); for int8 it is |x| (so -128 ranks highest). */
+/* Nearest fp16 (dtype 1) or bf16 (dtype 2) bit pattern to x, ties to even
+ * (the IEEE default rounding), written from the formats' definitions:
+ * fp16 = 1 sign, 5 exponent (bias 15), 10 fraction bits; bf16 = 1, 8 (bias
+ * 127), 7.  Values of magnitude at or beyond the point halfway between the
+ * largest finite value and the next power of two become Inf; NaN becomes
+ * the quiet NaN with the sign of x and the top fraction bit set. */
+uint32_t orc_round_to(double x, int dtype) {
+  int ebits, mbits;
+  if (dtype == ORC_F16) { ebits = 5; mbits = 10; }
+  else if (dtype == ORC_BF16) { ebits = 8; mbits = 7; }
+  else return 0;
+  const int bias = (1 << (ebits - 1)) - 1, emin = 1 - bias, emax = bias;
+  const uint32_t sign = signbit(x) ? 1u << (ebits + mbits) : 0u;
+  const uint32_t inf = ((1u << ebits) - 1u) << mbits;
+  if (isnan(x)) return sign | inf | (1u << (mbits - 1));
+  double a = fabs(x);
+  if (isinf(a)) return sign | inf;
+  if (a == 0.0) return sign;
+  /* quantum: spacing of representable values in the binade of a (the
+   * subnormal spacing below the smallest normal) */
+  int e;
+  frexp(a, &e);  /* a = f * 2^e, 0.5 <= f < 1, so floor(log2 a) = e - 1 */
+  int qe = (e - 1 < emin ? emin : e - 1) - mbits;
+  double y = ldexp(a, -qe);  /* exact: a power-of-two scaling */
+  double f = floor(y), d = y - f;
+  if (d > 0.5 || (d == 0.5 && fmod(f, 2.0) != 0.0)) f += 1.0;
+  double r = ldexp(f, qe);   /* the rounded magnitude, exact */
+  const double maxfin = ldexp(2.0 - ldexp(1.0, -mbits), emax);
+  if (r > maxfin) return sign | inf;
+  if (r < ldexp(1.0, emin)) /* subnormal (or zero): field 0, fraction r / 2^(emin - mbits) */
+    return sign | (uint32_t)ldexp(r, mbits - emin);
+  frexp(r, &e);
+  const int ex = e - 1;
+  const uint32_t frac = (uint32_t)(ldexp(r, mbits - ex) - ldexp(1.0, mbits));
+  return sign | ((uint32_t)(ex + bias) << mbits) | frac;
+}
+
 uint32_t orc_key(uint32_t bits, int dtype) {
   switch (dtype) {
     case ORC_F16: case ORC_BF16: return bits & 0x7FFFu;
@@ -210,12 +253,14 @@ static double* decode_table(int dtype) {
 
 /* Floating-point sparse product, straight from the compressed form:
  *   acc[i][j] = sum_c dec(vals[i][c]) * dec(B[4*(c/2) + code(i,c)][j])
- *   D[i][j]   = alpha * acc[i][j] + beta * C[i][j]   (C not read if beta == 0)
- * B is K x N row-major (N contiguous); C is M x N float32; D is M x N double.
- * If absD is not NULL it receives |alpha| * sum_c |a * b| + |beta * C|, the
- * scale used by the error bound of the comparison. */
+ *   D[i][j]   = alpha * acc[i][j] + beta * C[i][j] + bias[j]
+ * (C not read if beta == 0; no bias term if bias is NULL).
+ * B is K x N row-major (N contiguous); C is M x N, given as float32 values
+ * (a 16-bit C is passed widened, which is exact); D is M x N double.
+ * If absD is not NULL it receives |alpha| * sum_c |a * b| + |beta * C| +
+ * |bias|, the scale used by the error bound of the comparison. */
 int orc_gemm_f64(const void* vals, const uint32_t* meta, int a_type, const void* B, int b_type,
-                 const float* C, double* D, double* absD, int64_t M, int64_t N, int64_t K,
+                 const float* C, const float* bias, double* D, double* absD, int64_t M, int64_t N, int64_t K,
                  double alpha, double beta) {
   const int ea = orc_elem_size(a_type), eb = orc_elem_size(b_type);
   if (ea == 0 || eb == 0 || a_type == ORC_I8 || b_type == ORC_I8) return ORC_BAD_ARG;
@@ -244,6 +289,10 @@ int orc_gemm_f64(const void* vals, const uint32_t* meta, int a_type, const void*
         const double cv = (double)C[i * N + j];
         d += beta * cv;
         s += fabs(beta * cv);
+      }
+      if (bias) {
+        d += (double)bias[j];
+        s += fabs((double)bias[j]);
       }
       D[i * N + j] = d;
       if (absD) absD[i * N + j] = s;

@@ -16,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsp24.so")
 
 SP24_F16, SP24_BF16, SP24_I8, SP24_FP8_E4M3, SP24_BF8_E5M2 = 1, 2, 3, 4, 5
+SP24_F32, SP24_I32 = 6, 7  # output (C / D) types only
 SP24_LAYOUT_ROW, SP24_LAYOUT_KBLOCK = 0, 1
 SP24_B_KN, SP24_B_NK = 0, 1
 SP24_OK = 0
@@ -48,6 +49,8 @@ def lib():
         L.sp24_prune_compress.restype = I
         L.sp24_gemm.argtypes = [P, P, I, I, P, I, I, P, I64, I64, I64, F, F, P, SZ, P]
         L.sp24_gemm.restype = I
+        L.sp24_gemm_ex.argtypes = [P, P, I, I, P, I, I, P, I, P, I64, I64, I64, F, F, P, SZ, P]
+        L.sp24_gemm_ex.restype = I
         L.sp24_decompress.argtypes = [P, P, P, I64, I64, I, I, P]
         L.sp24_decompress.restype = I
         L.sp24_validate_meta.argtypes = [P, I64, I64, I, I, P, P]
@@ -83,6 +86,13 @@ def sp24_gemm(A_vals: int, meta: int, a_type: int, layout: int, B: int, b_type: 
               stream: int | None) -> int:
     return lib().sp24_gemm(A_vals, meta, a_type, layout, B, b_type, b_layout, C, M, N, K, alpha, beta, workspace,
                            workspace_bytes, stream)
+
+
+def sp24_gemm_ex(A_vals: int, meta: int, a_type: int, layout: int, B: int, b_type: int, b_layout: int, C: int,
+                 c_type: int, bias: int | None, M: int, N: int, K: int, alpha: float, beta: float,
+                 workspace: int | None, workspace_bytes: int, stream: int | None) -> int:
+    return lib().sp24_gemm_ex(A_vals, meta, a_type, layout, B, b_type, b_layout, C, c_type, bias, M, N, K, alpha,
+                              beta, workspace, workspace_bytes, stream)
 
 
 def sp24_decompress(A_vals: int, meta: int, A: int, M: int, K: int, dtype: int, layout: int,
@@ -166,13 +176,16 @@ def prune_compress(A, dtype: int | None = None, layout: int = SP24_LAYOUT_KBLOCK
 
 
 def gemm(A_vals, meta, B, C=None, alpha: float = 1.0, beta: float = 0.0, a_type: int | None = None,
-         b_type: int | None = None, layout: int | None = None, stream=None):
-    """D = alpha * expand(A_vals, meta) @ B + beta * C, written into C
+         b_type: int | None = None, layout: int | None = None, stream=None, out_dtype=None, bias=None):
+    """D = alpha * expand(A_vals, meta) @ B + beta * C (+ bias), written into C
     (allocated, uninitialised, when C is None and beta == 0).  ``layout``
     defaults to what the tensors' rank says: 2-D = ROW, 3-D = KBLOCK.
     B is K x N: either contiguous (SP24_B_KN) or the transpose of a
     contiguous N x K tensor, e.g. ``X.t()`` for activations X (SP24_B_NK).
-    Returns C."""
+    ``out_dtype`` (torch.float32 by default, or float16 / bfloat16; int32 for
+    int8 inputs) is the type of C / D, taken from C when it is given.
+    ``bias``: optional length-N float32 tensor added to every row (calls
+    sp24_gemm_ex).  Returns C."""
     import torch
     if a_type is None:
         a_type = dtype_code(A_vals.dtype)
@@ -192,18 +205,35 @@ def gemm(A_vals, meta, B, C=None, alpha: float = 1.0, beta: float = 0.0, a_type:
     if tuple(A_vals.shape) != vshape or tuple(meta.shape) != mshape:
         raise ValueError(f"compressed A has shapes {tuple(A_vals.shape)} / {tuple(meta.shape)}; "
                          f"K = {K} in this layout needs {vshape} / {mshape}")
-    out_dtype = torch.int32 if (a_type == SP24_I8 and b_type == SP24_I8) else torch.float32
+    is_int = a_type == SP24_I8 and b_type == SP24_I8
+    if out_dtype is None:
+        out_dtype = C.dtype if C is not None else (torch.int32 if is_int else torch.float32)
+    c_type = {torch.float32: SP24_F32, torch.float16: SP24_F16, torch.bfloat16: SP24_BF16,
+              torch.int32: SP24_I32}.get(out_dtype)
+    if c_type is None:
+        raise TypeError(f"unsupported output type {out_dtype}")
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs C")
         C = torch.empty((M, N), dtype=out_dtype, device=B.device)
+    elif C.dtype != out_dtype:
+        raise TypeError(f"C is {C.dtype}, output type is {out_dtype}")
     for t in (A_vals, meta, C):
         if not t.is_contiguous():
             raise ValueError("A_vals, meta and C must be contiguous")
-    st = sp24_gemm(A_vals.data_ptr(), meta.data_ptr(), a_type, layout, B.data_ptr(), b_type, b_layout, C.data_ptr(),
-                   M, N, K, float(alpha), float(beta), None, 0, _stream(stream))
+    if bias is not None and (bias.dtype != torch.float32 or not bias.is_contiguous() or bias.numel() != N):
+        raise ValueError("bias must be a contiguous float32 tensor of N values")
+    if bias is None and c_type == (SP24_I32 if is_int else SP24_F32):
+        st = sp24_gemm(A_vals.data_ptr(), meta.data_ptr(), a_type, layout, B.data_ptr(), b_type, b_layout,
+                       C.data_ptr(), M, N, K, float(alpha), float(beta), None, 0, _stream(stream))
+        what = "sp24_gemm"
+    else:
+        st = sp24_gemm_ex(A_vals.data_ptr(), meta.data_ptr(), a_type, layout, B.data_ptr(), b_type, b_layout,
+                          C.data_ptr(), c_type, None if bias is None else bias.data_ptr(), M, N, K, float(alpha),
+                          float(beta), None, 0, _stream(stream))
+        what = "sp24_gemm_ex"
     if st != SP24_OK:
-        raise Sp24Error(st, "sp24_gemm")
+        raise Sp24Error(st, what)
     return C
 
 

@@ -8,7 +8,8 @@ namespace sp24 {
 hipError_t launch_prune_compress(const void* A, void* vals, uint32_t* meta, int64_t M, int64_t K, int dtype,
                                  int layout, hipStream_t stream);
 hipError_t launch_gemm(int op, int layout, int b_layout, const void* A_vals, const uint32_t* meta, const void* B,
-                       void* C, int M, int N, int K, float alpha, float beta, hipStream_t stream);
+                       void* C, int M, int N, int K, float alpha, float beta, const float* bias, int out,
+                       hipStream_t stream);
 hipError_t launch_decompress(const void* vals, const uint32_t* meta, void* A, int64_t M, int64_t K, int dtype,
                              int layout, hipStream_t stream);
 hipError_t launch_validate(const uint32_t* meta, int64_t M, int64_t K, int dtype, int layout, uint64_t* bad,
@@ -96,11 +97,26 @@ int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, 
   return e == hipSuccess ? SP24_OK : SP24_ERR_LAUNCH;
 }
 
-int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, const void* B, int b_type,
-              int b_layout, void* C, int64_t M, int64_t N, int64_t K, float alpha, float beta, void* workspace,
-              size_t workspace_bytes, void* stream) {
+int sp24_gemm_ex(const void* A_vals, const uint32_t* meta, int a_type, int layout, const void* B, int b_type,
+                 int b_layout, void* C, int c_type, const float* bias, int64_t M, int64_t N, int64_t K, float alpha,
+                 float beta, void* workspace, size_t workspace_bytes, void* stream) {
   const int op = op_for(a_type, b_type);
   if (op < 0 || !layout_ok(layout) || (b_layout != SP24_B_KN && b_layout != SP24_B_NK)) return SP24_ERR_UNSUPPORTED;
+  // output type: int32 for int8 inputs (no bias), fp32 / fp16 / bf16 otherwise
+  int out;
+  if (op == sp24::OP_I8) {
+    if (c_type != SP24_I32 || bias) return SP24_ERR_UNSUPPORTED;
+    out = sp24::OUT_32;
+  } else if (c_type == SP24_F32) {
+    out = sp24::OUT_32;
+  } else if (c_type == SP24_F16) {
+    out = sp24::OUT_F16;
+  } else if (c_type == SP24_BF16) {
+    out = sp24::OUT_BF16;
+  } else {
+    return SP24_ERR_UNSUPPORTED;
+  }
+  const int ec = out == sp24::OUT_32 ? 4 : 2;
   if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
     return SP24_ERR_INVALID_VALUE;
   const int ea = esize(a_type), eb = esize(b_type);
@@ -117,16 +133,26 @@ int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, 
   if (M == 0 || N == 0) return SP24_OK;
   if (!C) return SP24_ERR_INVALID_VALUE;
   if (K > 0 && (!A_vals || !meta || !B)) return SP24_ERR_INVALID_VALUE;
-  if (!aligned16(C) || (K > 0 && (!aligned16(A_vals) || !aligned16(meta) || !aligned16(B))))
+  if (!aligned16(C) || (K > 0 && (!aligned16(A_vals) || !aligned16(meta) || !aligned16(B))) ||
+      (bias && !aligned16(bias)))
     return SP24_ERR_MISALIGNED;
-  const uint64_t c_bytes = (uint64_t)M * N * 4;
+  const uint64_t c_bytes = (uint64_t)M * N * ec;
   if (K > 0 && (overlap(C, c_bytes, A_vals, sp24_values_bytes(M, K, a_type, layout)) ||
                 overlap(C, c_bytes, meta, sp24_meta_bytes(M, K, a_type, layout)) ||
                 overlap(C, c_bytes, B, (uint64_t)K * N * eb)))
     return SP24_ERR_INVALID_VALUE;
+  if (bias && overlap(C, c_bytes, bias, (uint64_t)N * 4)) return SP24_ERR_INVALID_VALUE;
   const hipError_t e = sp24::launch_gemm(op, layout, b_layout, A_vals, meta, B, C, (int)M, (int)N, (int)K, alpha,
-                                         beta, static_cast<hipStream_t>(stream));
+                                         beta, bias, out, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SP24_OK : SP24_ERR_LAUNCH;
+}
+
+int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, const void* B, int b_type,
+              int b_layout, void* C, int64_t M, int64_t N, int64_t K, float alpha, float beta, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  const int c_type = op_for(a_type, b_type) == sp24::OP_I8 ? SP24_I32 : SP24_F32;
+  return sp24_gemm_ex(A_vals, meta, a_type, layout, B, b_type, b_layout, C, c_type, nullptr, M, N, K, alpha, beta,
+                      workspace, workspace_bytes, stream);
 }
 
 int sp24_decompress(const void* A_vals, const uint32_t* meta, void* A, int64_t M, int64_t K, int dtype, int layout,
@@ -168,6 +194,6 @@ const char* sp24_status_string(int status) {
   }
 }
 
-int sp24_version(void) { return 300; }
+int sp24_version(void) { return 400; }
 
 }  // extern "C"

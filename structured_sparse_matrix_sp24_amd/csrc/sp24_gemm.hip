@@ -1,4 +1,5 @@
-// sp24_gemm: D = alpha * expand(A_vals, meta) * B + beta * C on the gfx950
+// sp24_gemm: D = alpha * expand(A_vals, meta) * B + beta * C (+ bias, in
+// fp32, bf16 or fp16) on the gfx950
 // sparse matrix cores (v_smfmac_*_16x16x64 for 16-bit inputs, *_16x16x128 for
 // 8-bit inputs).
 //
@@ -313,7 +314,7 @@ template <int OP, int LAYOUT, int BL>
 __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __restrict__ A_vals,
                                                                  const char* __restrict__ meta,
                                                                  const char* __restrict__ B, void* C, int M, int N,
-                                                                 int K, float alpha, float beta, int tiles_m,
+                                                                 int K, Epilogue ep, int tiles_m,
                                                                  int tiles_n) {
   // One LDS object per stage.
   __shared__ __attribute__((aligned(1024))) char lS0[kLdsStage], lS1[kLdsStage], lS2[kLdsStage];
@@ -496,7 +497,8 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
     }
   }
 
-  // ---- epilogue: D = alpha * acc + beta * C  (int8: acc + C when beta == 1).
+  // ---- epilogue: D = alpha * acc + beta * C + bias, in the output type
+  // (int8: acc + C when beta == 1).
   // Each 16 x 64 slice of a wave goes through a per-wave LDS scratch (rows
   // padded to 80 words) so that every lane moves 16 contiguous bytes and each
   // row segment is 256 contiguous bytes.  N is a multiple of 8, so a 4-column
@@ -521,18 +523,9 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
       const f32x4 v = *(const SP24_LDS f32x4*)(scr + rr * 80 + (l & 15) * 4);
       const int row = row_base + tm * 16 + rr;
       if (row < M && col < N) {
-        const int64_t o = (int64_t)row * N + col;
         // streaming stores: the output is not re-read here, and letting it
         // allocate in the caches evicts the A and B data other tiles reuse
-        if constexpr (op_is_int(OP)) {
-          i32x4 d = __builtin_bit_cast(i32x4, v);
-          if (beta != 0.0f) d += __builtin_nontemporal_load((const i32x4*)((const int*)C + o));
-          __builtin_nontemporal_store(d, (i32x4*)((int*)C + o));
-        } else {
-          f32x4 d = v * alpha;
-          if (beta != 0.0f) d += beta * __builtin_nontemporal_load((const f32x4*)((const float*)C + o));
-          __builtin_nontemporal_store(d, (f32x4*)((float*)C + o));
-        }
+        store_out4<op_is_int(OP)>(C, (int64_t)row * N + col, col, v, ep);
       }
     }
   }
@@ -586,7 +579,7 @@ template <int OP, int LAYOUT, int D, int BL>
 __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const char* __restrict__ A_vals,
                                                                         const char* __restrict__ meta,
                                                                         const char* __restrict__ B, void* C, int M,
-                                                                        int N, int K, float alpha, float beta) {
+                                                                        int N, int K, Epilogue ep) {
   constexpr int KS = op_kstep(OP), ES = op_esize(OP), MB = meta_step_bytes<OP>();
   constexpr int SLOT = small_slot<D>();
   __shared__ __attribute__((aligned(1024))) char lB[kSmallWaves * D * SLOT];
@@ -776,76 +769,76 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
       int sum = 0;
       for (int ww = 0; ww < kSmallWaves; ++ww) sum += red[((ww * 4 + tn) * 4 + r) * 64 + lane];
       int* Dp = static_cast<int*>(C);
-      Dp[o] = beta != 0.0f ? sum + Dp[o] : sum;
+      Dp[o] = ep.beta != 0.0f ? sum + Dp[o] : sum;
     } else {
       float sum = 0.0f;
       for (int ww = 0; ww < kSmallWaves; ++ww) sum += __int_as_float(red[((ww * 4 + tn) * 4 + r) * 64 + lane]);
-      float* Dp = static_cast<float*>(C);
-      const float v = alpha * sum;
-      Dp[o] = beta != 0.0f ? v + beta * Dp[o] : v;
+      store_out1<false>(C, o, gcol, sum, ep);
     }
   }
 }
 
-// ---- K == 0: D = beta * C ---------------------------------------------------
+// ---- K == 0: D = beta * C (+ bias), in the output type -----------------------
 template <bool INT>
-__global__ void scale_c_kernel(void* C, int64_t n, float beta) {
+__global__ void scale_c_kernel(void* C, int64_t n, int N, Epilogue ep) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   if constexpr (INT) {
     int* D = static_cast<int*>(C);
-    D[i] = beta != 0.0f ? D[i] : 0;
+    D[i] = ep.beta != 0.0f ? D[i] : 0;
   } else {
-    float* D = static_cast<float*>(C);
-    D[i] = beta != 0.0f ? beta * D[i] : 0.0f;
+    // alpha * (empty sum) = +0, then beta * C and the bias as in store_out1
+    store_out1<false>(C, i, (int)(i % N), 0.0f, ep);
   }
 }
 
 template <int OP, int LAYOUT, int BL>
 static hipError_t launch_op(const void* A_vals, const uint32_t* meta, const void* B, void* C, int M, int N, int K,
-                            float alpha, float beta, hipStream_t stream) {
+                            const Epilogue& ep, hipStream_t stream) {
   const char* a = static_cast<const char*>(A_vals);
   const char* m = reinterpret_cast<const char*>(meta);
   const char* b = static_cast<const char*>(B);
   if (K == 0) {
     const int64_t n = (int64_t)M * N;
+    Epilogue e0 = ep;
+    e0.alpha = 0.0f;  // D = beta * C (+ bias) whatever alpha is, as BLAS does for K == 0
     hipLaunchKernelGGL((scale_c_kernel<op_is_int(OP)>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, C, n,
-                       beta);
+                       N, e0);
     return hipGetLastError();
   }
   if (N <= 64) {
     const dim3 grid((unsigned)((M + 15) / 16)), block(kSmallWaves * 64);
     if ((int64_t)op_kstep(OP) * N * op_esize(OP) <= small_bslice<4>())
-      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 4, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, alpha,
-                         beta);
+      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 4, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep);
     else
-      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 2, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, alpha,
-                         beta);
+      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 2, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep);
     return hipGetLastError();
   }
   const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
   hipLaunchKernelGGL((gemm_large8_kernel<OP, LAYOUT, BL>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads8), 0,
-                     stream, a, m, b, C, M, N, K, alpha, beta, tiles_m, tiles_n);
+                     stream, a, m, b, C, M, N, K, ep, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 template <int OP>
 static hipError_t launch_layout(int layout, int b_layout, const void* A_vals, const uint32_t* meta, const void* B,
-                                void* C, int M, int N, int K, float alpha, float beta, hipStream_t stream) {
+                                void* C, int M, int N, int K, const Epilogue& ep, hipStream_t stream) {
   if (layout == SP24_LAYOUT_KBLOCK) {
     if (b_layout == SP24_B_NK)
-      return launch_op<OP, SP24_LAYOUT_KBLOCK, SP24_B_NK>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
-    return launch_op<OP, SP24_LAYOUT_KBLOCK, SP24_B_KN>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+      return launch_op<OP, SP24_LAYOUT_KBLOCK, SP24_B_NK>(A_vals, meta, B, C, M, N, K, ep, stream);
+    return launch_op<OP, SP24_LAYOUT_KBLOCK, SP24_B_KN>(A_vals, meta, B, C, M, N, K, ep, stream);
   }
   if (b_layout == SP24_B_NK)
-    return launch_op<OP, SP24_LAYOUT_ROW, SP24_B_NK>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
-  return launch_op<OP, SP24_LAYOUT_ROW, SP24_B_KN>(A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+    return launch_op<OP, SP24_LAYOUT_ROW, SP24_B_NK>(A_vals, meta, B, C, M, N, K, ep, stream);
+  return launch_op<OP, SP24_LAYOUT_ROW, SP24_B_KN>(A_vals, meta, B, C, M, N, K, ep, stream);
 }
 
 hipError_t launch_gemm(int op, int layout, int b_layout, const void* A_vals, const uint32_t* meta, const void* B,
-                       void* C, int M, int N, int K, float alpha, float beta, hipStream_t stream) {
+                       void* C, int M, int N, int K, float alpha, float beta, const float* bias, int out,
+                       hipStream_t stream) {
+  const Epilogue ep{alpha, beta, bias, out};
 #define SP24_CASE(O) \
-  case O: return launch_layout<O>(layout, b_layout, A_vals, meta, B, C, M, N, K, alpha, beta, stream);
+  case O: return launch_layout<O>(layout, b_layout, A_vals, meta, B, C, M, N, K, ep, stream);
   switch (op) {
     SP24_CASE(OP_F16)
     SP24_CASE(OP_BF16)

@@ -108,6 +108,76 @@ __device__ __forceinline__ void waitcnt() {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
+// Epilogue of the product: D = round_out(alpha * acc + beta * C + bias[col]).
+// OUT_32 writes float32 (int32 for int8 inputs, where only beta in {0, 1}
+// and no bias are allowed); OUT_F16 / OUT_BF16 round the fp32 sum once, to
+// nearest even, and C is read in the same 16-bit type.
+enum OutType { OUT_32 = 0, OUT_F16 = 1, OUT_BF16 = 2 };
+struct Epilogue {
+  float alpha, beta;
+  const float* bias;  // N values or nullptr
+  int out;            // OutType
+};
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Four consecutive outputs of one row at element offset o, column col
+// (col % 4 == 0, all four inside N).  v = the fp32 accumulators.
+template <bool INT>
+__device__ __forceinline__ void store_out4(void* C, int64_t o, int col, f32x4 v, const Epilogue& ep) {
+  if constexpr (INT) {
+    i32x4 d = __builtin_bit_cast(i32x4, v);
+    if (ep.beta != 0.0f) d += __builtin_nontemporal_load((const i32x4*)((const int*)C + o));
+    __builtin_nontemporal_store(d, (i32x4*)((int*)C + o));
+  } else {
+    f32x4 d = v * ep.alpha;
+    if (ep.out == OUT_32) {
+      if (ep.beta != 0.0f) d += ep.beta * __builtin_nontemporal_load((const f32x4*)((const float*)C + o));
+      if (ep.bias) d += *(const f32x4*)(ep.bias + col);
+      __builtin_nontemporal_store(d, (f32x4*)((float*)C + o));
+    } else if (ep.out == OUT_F16) {
+      f16x4* p = (f16x4*)((_Float16*)C + o);
+      if (ep.beta != 0.0f) d += ep.beta * __builtin_convertvector(__builtin_nontemporal_load(p), f32x4);
+      if (ep.bias) d += *(const f32x4*)(ep.bias + col);
+      __builtin_nontemporal_store(__builtin_convertvector(d, f16x4), p);
+    } else {
+      bf16x4* p = (bf16x4*)((__bf16*)C + o);
+      if (ep.beta != 0.0f) d += ep.beta * __builtin_convertvector(__builtin_nontemporal_load(p), f32x4);
+      if (ep.bias) d += *(const f32x4*)(ep.bias + col);
+      __builtin_nontemporal_store(__builtin_convertvector(d, bf16x4), p);
+    }
+  }
+}
+
+// One output element (same arithmetic as store_out4).
+template <bool INT>
+__device__ __forceinline__ void store_out1(void* C, int64_t o, int col, float v, const Epilogue& ep) {
+  if constexpr (INT) {
+    int d = __float_as_int(v);
+    int* p = (int*)C + o;
+    *p = ep.beta != 0.0f ? d + *p : d;
+  } else {
+    float d = v * ep.alpha;
+    if (ep.out == OUT_32) {
+      float* p = (float*)C + o;
+      if (ep.beta != 0.0f) d += ep.beta * *p;
+      if (ep.bias) d += ep.bias[col];
+      *p = d;
+    } else if (ep.out == OUT_F16) {
+      _Float16* p = (_Float16*)C + o;
+      if (ep.beta != 0.0f) d += ep.beta * (float)*p;
+      if (ep.bias) d += ep.bias[col];
+      *p = (_Float16)d;
+    } else {
+      __bf16* p = (__bf16*)C + o;
+      if (ep.beta != 0.0f) d += ep.beta * (float)*p;
+      if (ep.bias) d += ep.bias[col];
+      *p = (__bf16)d;
+    }
+  }
+}
+
 // A copy of v the compiler cannot see through.  Addresses derived from it are
 // recomputed where they are used (a few VALU ops that co-issue with MFMA)
 // instead of being hoisted out of the K loop and held in registers.

@@ -125,6 +125,35 @@ def test_gemm_argument_errors(L):
     assert L.sp24_gemm(A, Mt, F16, L.SP24_LAYOUT_ROW, B, F16, 0, C, 64, 64, big_k, 1.0, 0.0, None, 0, None) == 2
 
 
+def test_gemm_ex_argument_errors(L):
+    P = 1 << 20
+    F16, BF, I8, E4, E5 = L.SP24_F16, L.SP24_BF16, L.SP24_I8, L.SP24_FP8_E4M3, L.SP24_BF8_E5M2
+    F32, I32 = L.SP24_F32, L.SP24_I32
+    A, Mt, B, C, bias = P, 2 * P, 3 * P, 8 * P, 16 * P
+    lay, kn = L.SP24_LAYOUT_KBLOCK, L.SP24_B_KN
+
+    def g(at, bt, ct, bi, M=0, alpha=1.0, beta=0.0, c=C):
+        return L.sp24_gemm_ex(A, Mt, at, lay, B, bt, kn, c, ct, bi, M, 64, 64, alpha, beta, None, 0, None)
+    # allowed output types pass validation up to the launch (M == 0)
+    for at, bt in [(F16, F16), (BF, BF), (E4, E5), (E5, E5)]:
+        for ct in (F32, F16, BF):
+            assert g(at, bt, ct, None) == 0
+            assert g(at, bt, ct, bias) == 0
+    assert g(I8, I8, I32, None) == 0
+    # int8 writes int32 only, without a bias; float inputs never write int32
+    assert g(I8, I8, F32, None) == 2
+    assert g(I8, I8, F16, None) == 2
+    assert g(I8, I8, I32, bias) == 2
+    assert g(F16, F16, I32, None) == 2
+    assert g(F16, F16, E4, None) == 2
+    assert g(F16, F16, 99, None) == 2
+    # misaligned bias, bias overlapping C
+    assert g(F16, F16, F16, bias + 4, M=64) == 3
+    assert g(F16, F16, F16, C + 64 * 64, M=64) == 1        # bias is the last bytes of a 64x64 fp16 C
+    # C of a 16-bit output is half the bytes: a bias right after it does not overlap
+    assert g(F16, F16, F16, C + 64 * 64 * 2, M=0) == 0
+
+
 def test_decompress_and_validate_argument_errors(L):
     d, v = L.sp24_decompress, L.sp24_validate_meta
     KB, ROW, F16 = L.SP24_LAYOUT_KBLOCK, L.SP24_LAYOUT_ROW, L.SP24_F16

@@ -292,6 +292,99 @@ def test_gemm_K_zero(pkg, layout):
     assert (C == 1.5).all()
 
 
+# ---- 16-bit output and bias (sp24_gemm_ex) ---------------------------------------
+OUT_T = {wl.F16: torch.float16, wl.BF16: torch.bfloat16}
+
+
+def grid_spacing(x, dtype):
+    """Spacing of the fp16 / bf16 grid at |x| (the subnormal spacing below the
+    smallest normal value)."""
+    mb, emin = (10, -14) if dtype == wl.F16 else (7, -126)
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** emin)))
+    return np.exp2(e - mb)
+
+
+def run_gemm_ex(pkg, vals, meta, a_type, B_bits, b_type, C_dev, out_dtype, bias, alpha, beta, b_layout=KN,
+                layout=KBLOCK):
+    v, m = in_layout(vals, meta, a_type, layout)
+    V = to_dev(v, a_type)
+    Mt = torch.from_numpy(np.ascontiguousarray(m).view(np.int32)).to(DEV)
+    B = b_on_dev(B_bits, b_type, b_layout)
+    bt = None if bias is None else torch.from_numpy(bias).to(DEV)
+    D = pkg.gemm(V, Mt, B, C_dev, alpha=alpha, beta=beta, a_type=a_type, b_type=b_type, layout=layout,
+                 out_dtype=out_dtype, bias=bt)
+    torch.cuda.synchronize()
+    return D
+
+
+@pytest.mark.parametrize("b_layout", [KN, NK])
+@pytest.mark.parametrize("with_bias", [False, True])
+@pytest.mark.parametrize("N", [32, 272])
+@pytest.mark.parametrize("a_type,b_type", [(wl.F16, wl.F16), (wl.BF16, wl.BF16), (wl.E4M3, wl.E5M2)])
+@pytest.mark.parametrize("out", [wl.F16, wl.BF16])
+def test_gemm_out16_bias(pkg, out, a_type, b_type, N, with_bias, b_layout):
+    """D = round16(alpha * A B + beta * C + bias): within the fp32 bound of the
+    oracle's exact value plus one step of the output grid."""
+    _say(f"gemm 16-bit out={out} a={a_type} N={N} bias={with_bias} b_layout={b_layout}")
+    M, K = 130, 224
+    c = wl.random_case(31, M, N, K, a_type, b_type, beta=1.0)
+    vals, meta = oracle.prune_compress(c.A, a_type)
+    rng = np.random.default_rng(7)
+    bias = rng.standard_normal(N).astype(np.float32) if with_bias else None
+    C16 = torch.from_numpy(c.C).to(OUT_T[out])            # C held in the output type
+    C32 = C16.to(torch.float32).numpy()                    # exactly its values, for the oracle
+    D = run_gemm_ex(pkg, vals, meta, a_type, c.B, b_type, C16.to(DEV), OUT_T[out], bias, -0.5, 1.5, b_layout)
+    got = oracle.decode(D.view(torch.int16).cpu().numpy().view(np.uint16), out)
+    ref, S = oracle.gemm_f64(vals, meta, a_type, c.B, b_type, C32, alpha=-0.5, beta=1.5, bias=bias)
+    err = np.abs(got - ref)
+    assert (err <= 1e-4 * S + 1e-6 + grid_spacing(ref, out)).all(), f"worst {np.max(err - 1e-4 * S):.3g}"
+    # where the exact value is far from a rounding boundary the bits are the
+    # oracle's rounding.  16-bit inputs: products are exact in fp32 and an
+    # fp32 sum of at most K/32 + 4 terms (k-steps, then the epilogue's) is off
+    # by less than (K/32 + 4) * 2^-24 * S.  8-bit float inputs: the sparse
+    # units flush bf8 subnormal inputs and truncate tiny mixed products, so
+    # only the parity bound itself applies there.
+    t = ref / grid_spacing(ref, out)
+    fp32_err = (K / 32 + 4) * 2.0 ** -24 * S if wl.ESIZE[a_type] == 2 else 1e-4 * S + 1e-6
+    far = (np.abs(t - np.round(t)) < 0.25) & (fp32_err < 0.1 * grid_spacing(ref, out))
+    if wl.ESIZE[a_type] == 2:
+        assert far.mean() > 0.3
+    exp_bits = oracle.round_to(ref[far], out)
+    assert np.array_equal(D.view(torch.int16).cpu().numpy().view(np.uint16)[far], exp_bits)
+
+
+@pytest.mark.parametrize("N", [48, 320])
+def test_gemm_bias_f32_out(pkg, N):
+    _say(f"gemm bias fp32 out N={N}")
+    c = wl.random_case(32, 96, N, 160, wl.BF16, wl.BF16, beta=1.0)
+    vals, meta = oracle.prune_compress(c.A, wl.BF16)
+    bias = np.random.default_rng(9).standard_normal(N).astype(np.float32) * 10
+    D = run_gemm_ex(pkg, vals, meta, wl.BF16, c.B, wl.BF16, torch.from_numpy(c.C).to(DEV), torch.float32, bias,
+                    0.25, 2.0).cpu().numpy().astype(np.float64)
+    ref, S = oracle.gemm_f64(vals, meta, wl.BF16, c.B, wl.BF16, c.C, alpha=0.25, beta=2.0, bias=bias)
+    assert (np.abs(D - ref) <= 1e-4 * S + 1e-6).all()
+
+
+@pytest.mark.parametrize("out", [wl.F16, wl.BF16])
+def test_gemm_K_zero_out16_bias(pkg, out):
+    """K = 0: D = round16(beta * C + bias) whatever alpha is."""
+    M, N = 8, 64
+    rng = np.random.default_rng(5)
+    C16 = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)).to(OUT_T[out])
+    bias = rng.standard_normal(N).astype(np.float32)
+    vs, ms = pkg.compressed_shapes(M, 0, pkg.SP24_F16, KBLOCK)
+    V = torch.empty(vs, dtype=torch.float16, device=DEV)
+    Mt = torch.empty(ms, dtype=torch.int32, device=DEV)
+    B = torch.empty((0, N), dtype=torch.float16, device=DEV)
+    Cd = C16.to(DEV)
+    pkg.gemm(V, Mt, B, Cd, alpha=float("inf"), beta=0.5, layout=KBLOCK, out_dtype=OUT_T[out],
+             bias=torch.from_numpy(bias).to(DEV))
+    torch.cuda.synchronize()
+    ref = 0.5 * C16.to(torch.float64).numpy() + bias.astype(np.float64)[None, :]
+    got = oracle.decode(Cd.view(torch.int16).cpu().numpy().view(np.uint16), out)
+    assert (np.abs(got - ref) <= 1e-6 * np.abs(ref) + grid_spacing(ref, out)).all()
+
+
 def test_gemm_gpu_compressed_input(pkg):
     """Compress on the GPU and multiply the result directly."""
     _say("gemm on GPU-compressed input")

@@ -12,7 +12,10 @@
   * product: dense float64 / int64 matmul of the decompressed matrix (library
     routine), identity B (the pages' verification trick: "RDNA4 dense WMMA
     builtins", section on the scalar fallback, checks C == A with B = I),
-    one-hot brute force on a 16 x 16 x 32 tile, and epilogue special cases.
+    one-hot brute force on a 16 x 16 x 32 tile, and epilogue special cases;
+  * rounding to a 16-bit output: every fp16 value and tie against numpy's
+    float64 -> float16 cast, float32 inputs against torch's bfloat16
+    conversion, and tie closed forms.
 """
 import json
 import os
@@ -285,8 +288,70 @@ def test_epilogue_special_cases(orc):
     Cnan = np.full((8, 8), np.nan, np.float32)
     Dn = np.empty((8, 8), np.float64)
     rc = lib.orc_gemm_f64(vals.ctypes.data, meta.ctypes.data, wl.F16, c.B.ctypes.data, wl.F16,
-                          Cnan.ctypes.data, Dn.ctypes.data, None, 8, 8, 32, 1.0, 0.0)
+                          Cnan.ctypes.data, None, Dn.ctypes.data, None, 8, 8, 32, 1.0, 0.0)
     assert rc == 0 and not np.isnan(Dn).any()
+
+
+def test_bias_is_added_per_column(orc):
+    """D with a bias = D without it + bias[j] in every row (and |bias| in the
+    error scale); checked against the dense product, as the product pins do."""
+    c = wl.random_case(21, 12, 40, 64, wl.BF16, wl.BF16, beta=1.0)
+    vals, meta = orc.prune_compress(c.A, wl.BF16)
+    bias = np.random.default_rng(3).standard_normal(40).astype(np.float32)
+    D, S = orc.gemm_f64(vals, meta, wl.BF16, c.B, wl.BF16, c.C, alpha=-1.5, beta=0.5, bias=bias)
+    Ad = torch.from_numpy(torch_decode(orc.decompress(vals, meta, wl.BF16), wl.BF16))
+    Bd = torch.from_numpy(torch_decode(c.B, wl.BF16))
+    ref = -1.5 * (Ad @ Bd).numpy() + 0.5 * c.C.astype(np.float64) + bias.astype(np.float64)[None, :]
+    absref = 1.5 * (Ad.abs() @ Bd.abs()).numpy() + 0.5 * np.abs(c.C.astype(np.float64)) + \
+        np.abs(bias.astype(np.float64))[None, :]
+    assert np.abs(D - ref).max() <= 1e-12 * absref.max()
+    assert np.allclose(S, absref, rtol=1e-12, atol=0)
+
+
+# ---- rounding to a 16-bit output --------------------------------------------------
+def _f16_grid_and_ties():
+    """Every finite fp16 value, and every midpoint between neighbours (the ties),
+    and points a hair either side of each midpoint."""
+    v = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mid = (v[:-1] + v[1:]) / 2
+    eps = np.abs(mid) * 2.0 ** -40 + 2.0 ** -1000
+    return np.concatenate([v, mid, mid - eps, mid + eps])
+
+
+def test_round_to_f16_matches_numpy(orc):
+    """fp16: numpy's float64 -> float16 cast rounds directly, to nearest even
+    (a library routine); checked on every value, every tie and its neighbours,
+    both signs, random magnitudes from far below the subnormals to far beyond
+    the largest finite value, and the special values."""
+    rng = np.random.default_rng(0)
+    x = _f16_grid_and_ties()
+    x = np.concatenate([x, -x, np.exp2(rng.uniform(-30, 20, 20000)) * rng.choice([-1.0, 1.0], 20000),
+                        [0.0, -0.0, np.inf, -np.inf, 65504.0, 65519.999, 65520.0, 65536.0, 2.0 ** -25,
+                         3 * 2.0 ** -26, 2.0 ** -26]])
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(orc.round_to(x, orc.F16), ref)
+    nan = orc.round_to(np.array([np.nan, -np.nan]), orc.F16)
+    assert all((b & 0x7C00) == 0x7C00 and (b & 0x3FF) != 0 for b in nan)
+
+
+def test_round_to_bf16_matches_torch(orc):
+    """bf16: torch's CPU float32 -> bfloat16 conversion rounds to nearest even
+    (a library routine).  The inputs are float32 values (so that the check
+    does not depend on how torch narrows float64): random bit patterns over
+    the whole finite range, every tie of the bf16 grid around a spread of
+    exponents, and its neighbours."""
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 0x7F800000, 200000, dtype=np.int64).astype(np.uint32)
+    hi = np.arange(0, 0x7F80, 7, dtype=np.uint32) << 16
+    ties = np.concatenate([hi | 0x8000, hi | 0x7FFF, hi | 0x8001, (hi + 0x10000) | 0x8000])
+    f32 = np.concatenate([bits, ties, np.array([0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF, 1, 0x8000], np.uint32)])
+    f32 = np.concatenate([f32, f32 | np.uint32(0x80000000)]).view(np.float32)
+    ref = torch.from_numpy(f32.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.round_to(f32.astype(np.float64), orc.BF16), ref)
+    # closed forms: ties go to the even neighbour
+    one = orc.round_to(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -30]), orc.BF16)
+    assert list(one) == [0x3F80, 0x3F82, 0x3F81]
 
 
 def test_bad_arguments_rejected(orc):
