@@ -211,52 +211,78 @@ struct TileArgs {
   int Mp;          // KBLOCK: metadata rows per block (M rounded up to 128)
 };
 
-// Buffer resources and LDS base of this wave's loads for k-step j (scalar
-// work only, computed ahead of the phase that issues the loads).  Loads are
-// issued for every j, also past the last step: those get empty buffer ranges
-// and read nothing, which keeps the per-step load count uniform.  B rows
-// past K and rows past M read as zero through the buffer range check.
+// Everything this wave's loads of k-step j need, computed ahead of the phase
+// that issues them: buffer resources, the LDS base of the stage, the step's
+// offset inside a row (ROW layout; a scalar, passed as the load's SGPR
+// offset) and the per-lane offsets.  Loads are issued for every j, also past
+// the last step: those get empty buffer ranges and read nothing, which keeps
+// the per-step load count uniform.  B rows past K and rows past M read as
+// zero through the buffer range check.  In a step that ends past K, lanes
+// past the row end are masked (MASK; the K loop runs the steps that need no
+// masking in a copy without it, since vector ALU work next to the MFMAs
+// measured a few percent of the kernel time).
 struct DmaStep {
   i32x4 rA, rB, rM;
-  uint32_t lds;      // LDS byte address of the stage
-  uint32_t offA;     // ROW layout: byte offset of the step inside a row of A
-  uint32_t offM;     // ROW layout: same for the metadata
-  bool tail;         // the step ends past K (masking needed)
-  int64_t validA;    // bytes of the step inside a row of A
-  int64_t validM;    // ROW layout: bytes of the step inside a metadata row
-  int64_t validB;    // N x K: bytes of the step inside a row of B
+  uint32_t lds;     // LDS byte address of the stage
+  uint32_t sA, sM;  // ROW layout: byte offset of the step inside a row of A / of metadata
+  uint32_t vA[2];   // A: per-lane offsets of the two pieces
+  uint32_t vM[2];   // metadata: per-lane offsets
+  uint32_t vB[4];   // B: per-lane offsets
 };
 
-template <int OP, int LAYOUT, int BL>
-__device__ __forceinline__ DmaStep make_dma_step(SP24_LDS char* st, const TileArgs& ta, int j) {
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
+template <int OP, int LAYOUT, int BL, bool MASK>
+__device__ __forceinline__ DmaStep make_dma_step(SP24_LDS char* st, const TileArgs& ta, const LaneConsts8& lc,
+                                                 int j) {
   constexpr int KS = op_kstep(OP), ES = op_esize(OP), MB = meta_step_bytes<OP>();
   DmaStep d;
   d.lds = lds_addr(st);
-  d.tail = j >= ta.nfull;
-  d.validA = ta.rowA - (int64_t)j * 64;
-  d.validM = ta.rowM - (int64_t)j * MB;
   if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK) {
     const bool in = j < ta.nsteps;
     d.rA = make_rsrc4(ta.A_vals + ((int64_t)j * ta.M + ta.m0) * 64, in ? (uint64_t)(ta.M - ta.m0) * 64 : 0u);
     d.rM = make_rsrc4(ta.meta + ((int64_t)j * ta.Mp + ta.m0) * MB, in ? (uint64_t)(ta.Mp - ta.m0) * MB : 0u);
-    d.offA = d.offM = 0;
+    d.sA = d.sM = 0;
   } else {
     d.rA = ta.rA;
     d.rM = ta.rM;
-    d.offA = (uint32_t)(j * 64);
-    d.offM = (uint32_t)(j * MB);
+    d.sA = (uint32_t)(j * 64);
+    d.sM = (uint32_t)(j * MB);
   }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    d.vA[i] = lc.voA[i];
+    d.vM[i] = lc.voM[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d.vB[i] = lc.voB[i];
+  int64_t validB = 0;
   if constexpr (BL == SP24_B_NK) {
     // the tile's columns from byte j*128 on: rows past N fall outside the
     // range, the end of the row in the last step is masked per lane
-    d.validB = ta.ldbk - (int64_t)j * 128;
+    validB = ta.ldbk - (int64_t)j * 128;
     const int64_t rows = min(ta.N - ta.n0, kBN);
     d.rB = make_rsrc4(ta.B + (int64_t)ta.n0 * ta.ldbk + (int64_t)j * 128,
-                      d.validB > 0 ? (uint64_t)(rows * ta.ldbk - (int64_t)j * 128) : 0u);
+                      validB > 0 ? (uint64_t)(rows * ta.ldbk - (int64_t)j * 128) : 0u);
   } else {
     const int64_t start = ((int64_t)j * KS * ta.N + ta.n0) * ES;
     d.rB = make_rsrc4(ta.B + start, start < ta.btotal ? (uint64_t)(ta.btotal - start) : 0u);
-    d.validB = 0;
+  }
+  if constexpr (MASK) {
+    if (j >= ta.nfull) {
+      const int l = lane_id();
+      if (16 * (l >> 4) >= ta.rowA - (int64_t)j * 64) d.vA[0] = d.vA[1] = kOOB;
+      if constexpr (LAYOUT == SP24_LAYOUT_ROW)
+        if ((ES == 2 ? 4 * (l & 1) : 4 * (l & 3)) >= ta.rowM - (int64_t)j * MB) d.vM[0] = d.vM[1] = kOOB;
+      if constexpr (BL == SP24_B_NK) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * lc.chB[i] >= validB) d.vB[i] = kOOB;
+      }
+    }
   }
   return d;
 }
@@ -265,32 +291,17 @@ __device__ __forceinline__ DmaStep make_dma_step(SP24_LDS char* st, const TileAr
 //   P = 0, 1   A values, tile rows 16*(2w+P) .. +16 (64 B each);
 //   P = 2..5   B, 1 KiB block 4w+P-2 of the step;
 //   P = 6, 7   metadata piece P-6 (8-bit inputs load two, 16-bit one).
-// In a step that ends past K (the last one when K is not a multiple of KS,
-// and those past the end) lanes past the row end are masked.
+// A masked lane's offset kOOB plus the step offset stays above every range.
 template <int OP, int LAYOUT, int BL, int P>
-__device__ __forceinline__ void dma_piece(const DmaStep& d, const LaneConsts8& lc, int w) {
+__device__ __forceinline__ void dma_piece(const DmaStep& d, int w) {
   constexpr int ES = op_esize(OP);
   if constexpr (P < 2) {
-    uint32_t off = lc.voA[P] + d.offA;
-    if (d.tail) {
-      if (16 * (lane_id() >> 4) >= d.validA) off = kOOB;
-    }
-    dma16_asm(d.rA, d.lds + (w * 2 + P) * 1024, off, 0u);
+    dma16_asm(d.rA, d.lds + (w * 2 + P) * 1024, d.vA[P], d.sA);
   } else if constexpr (P < 6) {
-    uint32_t off = lc.voB[P - 2];
-    if constexpr (BL == SP24_B_NK)
-      if (d.tail && 16 * lc.chB[P - 2] >= d.validB) off = kOOB;
-    dma16_asm(d.rB, d.lds + kLdsA + (w * 4 + P - 2) * 1024, off, 0u);
+    dma16_asm(d.rB, d.lds + kLdsA + (w * 4 + P - 2) * 1024, d.vB[P - 2], 0u);
   } else {
     constexpr int i = P - 6;
-    uint32_t off = lc.voM[i] + d.offM;
-    if constexpr (LAYOUT == SP24_LAYOUT_ROW) {
-      if (d.tail) {
-        const int l = lane_id();
-        if ((ES == 2 ? 4 * (l & 1) : 4 * (l & 3)) >= d.validM) off = kOOB;
-      }
-    }
-    dma4_asm(d.rM, d.lds + kLdsA + kLdsB + (ES == 2 ? w * 256 : w * 512 + i * 256), off, 0u);
+    dma4_asm(d.rM, d.lds + kLdsA + kLdsB + (ES == 2 ? w * 256 : w * 512 + i * 256), d.vM[i], d.sM);
   }
 }
 
@@ -417,15 +428,15 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   };
   // All loads of this wave's share of step j, back to back (pipeline fill).
   auto dma_all = [&](int j) {
-    const DmaStep d = make_dma_step<OP, LAYOUT, BL>(st(j % 3), ta, j);
-    dma_piece<OP, LAYOUT, BL, 0>(d, lc, w);
-    dma_piece<OP, LAYOUT, BL, 1>(d, lc, w);
-    dma_piece<OP, LAYOUT, BL, 2>(d, lc, w);
-    dma_piece<OP, LAYOUT, BL, 3>(d, lc, w);
-    dma_piece<OP, LAYOUT, BL, 4>(d, lc, w);
-    dma_piece<OP, LAYOUT, BL, 5>(d, lc, w);
-    dma_piece<OP, LAYOUT, BL, 6>(d, lc, w);
-    if constexpr (L == 8) dma_piece<OP, LAYOUT, BL, 7>(d, lc, w);
+    const DmaStep d = make_dma_step<OP, LAYOUT, BL, true>(st(j % 3), ta, lc, j);
+    dma_piece<OP, LAYOUT, BL, 0>(d, w);
+    dma_piece<OP, LAYOUT, BL, 1>(d, w);
+    dma_piece<OP, LAYOUT, BL, 2>(d, w);
+    dma_piece<OP, LAYOUT, BL, 3>(d, w);
+    dma_piece<OP, LAYOUT, BL, 4>(d, w);
+    dma_piece<OP, LAYOUT, BL, 5>(d, w);
+    dma_piece<OP, LAYOUT, BL, 6>(d, w);
+    if constexpr (L == 8) dma_piece<OP, LAYOUT, BL, 7>(d, w);
   };
   // Staging phase: the fragments of step jr.
   auto stage_phase = [&](int jr) {
@@ -452,15 +463,15 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
         for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = smfmac16<OP>(acc[tm][tn], f.a[tm], f.b[tn], f.idxv[tm >> 2][tm & 3]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (tm == 0) dma_piece<OP, LAYOUT, BL, 0>(d, lc, w);
-      if (tm == 1) dma_piece<OP, LAYOUT, BL, 2>(d, lc, w);
-      if (tm == 2) dma_piece<OP, LAYOUT, BL, 3>(d, lc, w);
-      if (tm == 3) dma_piece<OP, LAYOUT, BL, 1>(d, lc, w);
-      if (tm == 4) dma_piece<OP, LAYOUT, BL, 4>(d, lc, w);
-      if (tm == 5) dma_piece<OP, LAYOUT, BL, 5>(d, lc, w);
-      if (tm == 6) dma_piece<OP, LAYOUT, BL, 6>(d, lc, w);
+      if (tm == 0) dma_piece<OP, LAYOUT, BL, 0>(d, w);
+      if (tm == 1) dma_piece<OP, LAYOUT, BL, 2>(d, w);
+      if (tm == 2) dma_piece<OP, LAYOUT, BL, 3>(d, w);
+      if (tm == 3) dma_piece<OP, LAYOUT, BL, 1>(d, w);
+      if (tm == 4) dma_piece<OP, LAYOUT, BL, 4>(d, w);
+      if (tm == 5) dma_piece<OP, LAYOUT, BL, 5>(d, w);
+      if (tm == 6) dma_piece<OP, LAYOUT, BL, 6>(d, w);
       if constexpr (L == 8)
-        if (tm == 7) dma_piece<OP, LAYOUT, BL, 7>(d, lc, w);
+        if (tm == 7) dma_piece<OP, LAYOUT, BL, 7>(d, w);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -474,27 +485,36 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   // The buffer resources of the loads a matrix phase issues are computed
   // during the staging phase before it, so the matrix phase only sets the LDS
   // address and issues each load between its MFMAs.
+  // Iterations k < kfull load only steps that end inside K (k + 3 < nfull)
+  // and run without the tail masking.
+  const int kfull = max(0, min(nsteps, ta.nfull - 3));
   if (g0) {
     phase_end<L>();  // this wave's share of step 0 has landed
     stage_phase(0);
-    DmaStep d = make_dma_step<OP, LAYOUT, BL>(st(2), ta, 2);
-    for (int k = 0; k < nsteps; ++k) {
+    DmaStep d = make_dma_step<OP, LAYOUT, BL, true>(st(2), ta, lc, 2);
+    auto iter = [&](int k, auto mask) {
       mfma_phase(d);              // phase 2k: step k, loads of step k+2
       phase_end<L>();             // this wave's share of step k+1 has landed
       stage_phase(k + 1);         // phase 2k+1
-      d = make_dma_step<OP, LAYOUT, BL>(st((k + 3) % 3), ta, k + 3);
+      d = make_dma_step<OP, LAYOUT, BL, decltype(mask)::value>(st((k + 3) % 3), ta, lc, k + 3);
       phase_end<63>();            // the reads of step k+1 are done
-    }
+    };
+    int k = 0;
+    for (; k < kfull; ++k) iter(k, BoolC<false>{});
+    for (; k < nsteps; ++k) iter(k, BoolC<true>{});
   } else {
     dma_all(2);
     phase_end<2 * L>();
-    for (int k = 0; k < nsteps; ++k) {
+    auto iter = [&](int k, auto mask) {
       stage_phase(k);             // phase 2k
-      const DmaStep d = make_dma_step<OP, LAYOUT, BL>(st(k % 3), ta, k + 3);
+      const DmaStep d = make_dma_step<OP, LAYOUT, BL, decltype(mask)::value>(st(k % 3), ta, lc, k + 3);
       phase_end<L>();             // this wave's share of step k+1 has landed, the reads of step k are done
       mfma_phase(d);              // phase 2k+1: step k, loads of step k+3
       phase_end<63>();
-    }
+    };
+    int k = 0;
+    for (; k < kfull; ++k) iter(k, BoolC<false>{});
+    for (; k < nsteps; ++k) iter(k, BoolC<true>{});
   }
 
   // ---- epilogue: D = alpha * acc + beta * C + bias, in the output type
