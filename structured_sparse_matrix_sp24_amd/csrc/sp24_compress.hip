@@ -14,10 +14,8 @@
 // whole 16-byte chunks with consecutive lanes on consecutive chunks, so every
 // wave instruction (load and store) is one contiguous span.  No MFMA, no LDS:
 // the kernel is bound by HBM bandwidth.  A is read with non-temporal loads
-// (it is not reused); the outputs are written with ordinary stores so they
-// stay in the caches for the product that usually follows (measured: the
-// 8192^3 fp16 product right after the compress ran 7 % faster than with
-// non-temporal stores here, and the compress itself 4 % faster).
+// (it is not reused); the outputs are written with ordinary stores, which
+// measured about 5 % faster than non-temporal ones for the 8192^2 fp16 A.
 //
 // The K-blocked output layout (one k-step of the GEMM = KB dense columns per
 // block, all M rows of a block stored together) uses a 2-D mapping instead:
