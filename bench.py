@@ -5,7 +5,10 @@ One step = sp24_prune_compress(A) followed by sp24_gemm(A_vals, meta, B) on a
 seeded synthetic workload (default: fp16, M = N = K = 8192, A and B ~ N(0,1),
 A pruned to 2:4 by the compress kernel, fp32 output, beta = 0).  Inputs are
 resident in HBM before the timed region; the timed region is exactly --steps
-steps bracketed by torch.cuda.synchronize().
+steps bracketed by torch.cuda.synchronize().  Before the --warmup steps the
+step runs untimed for --settle-s seconds (default 0.2) so the GPU's clocks
+have left their idle state: with only a few milliseconds of warm-up the
+timed steps measured about 7 % slower than in steady state.
 
 Prints ONE JSON line: value = dense-equivalent TFLOP/s of the whole step
 (2*M*N*K per step / step time); `roofline` describes the dominant kernel
@@ -118,6 +121,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-s", type=float, default=0.2,
+                    help="untimed seconds of steps before the warm-up steps (clock ramp)")
     ap.add_argument("--workload", default="f16_8192", choices=sorted(WORKLOADS))
     ap.add_argument("--layout", default="kblock", choices=["kblock", "row"],
                     help="compressed layout the step writes and the GEMM reads")
@@ -194,6 +199,14 @@ def main():
         if C0 is not None:  # beta != 0: keep each step's C input identical
             C.copy_(C0)
 
+    # clock settle: untimed steps for about --settle-s seconds, then the warm-up steps
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(8):
+            reset_c()
+            compress()
+            gemm()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         reset_c()
         compress()
