@@ -139,19 +139,19 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kernel(const 
 // (1 or 2 KiB, contiguous) is written with 16-byte stores.
 constexpr int kKbRowsPerTile = 128;
 
-// Blocks per workgroup: 16-bit types take 4 (each row's 512 contiguous bytes
-// are read by 32 lanes), 8-bit types 1 (their metadata is twice as large and
-// the staging writes collide in LDS with more blocks).
-template <int ES>
-__host__ __device__ constexpr int kb_blocks_per_wg() { return ES == 2 ? 4 : 1; }
+// Blocks per workgroup (NB): 16-bit types take 4 (each row's 512 contiguous
+// bytes are read by 32 lanes) when that still gives at least 1024
+// workgroups, else 1 (a 4096 x 4096 A then compresses in 14.5 us instead of
+// 16.6 us); 8-bit types always 1 (their metadata is twice as large and the
+// staging writes collide in LDS with more blocks).
+constexpr int64_t kKbMinWorkgroups = 1024;
 
-template <int ES, bool INT>
+template <int ES, bool INT, int NB>
 __global__ __launch_bounds__(kCompressThreads) void prune_compress_kblock_kernel(const char* __restrict__ A,
                                                                                    char* __restrict__ vals,
                                                                                    char* __restrict__ meta,
                                                                                    int64_t M, int64_t K,
                                                                                    uint32_t nblk) {
-  constexpr int NB = kb_blocks_per_wg<ES>();
   constexpr int MB = ES == 2 ? 8 : 16;         // metadata bytes per row per block
   constexpr int CE = 16 / ES;                   // dense elements per chunk
   constexpr int GB = 128 * MB;                  // metadata bytes of one 128-row group per block
@@ -232,17 +232,22 @@ hipError_t launch_prune_compress(const void* A, void* vals, uint32_t* meta, int6
     const int64_t kb = es == 2 ? 64 : 128;
     const int64_t nblk = (K + kb - 1) / kb;
     const int64_t row_tiles = (M + kKbRowsPerTile - 1) / kKbRowsPerTile;
-    const int64_t nwb = (nblk + (es == 2 ? kb_blocks_per_wg<2>() : kb_blocks_per_wg<1>()) - 1) /
-                        (es == 2 ? kb_blocks_per_wg<2>() : kb_blocks_per_wg<1>());
+    const int nb_per_wg = (es == 2 && row_tiles * ((nblk + 3) / 4) >= kKbMinWorkgroups) ? 4 : 1;
+    const int64_t nwb = (nblk + nb_per_wg - 1) / nb_per_wg;
     if (row_tiles * nwb > 0x7FFFFFFFll) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(row_tiles * nwb));
     const char* a = static_cast<const char*>(A);
     char* v = static_cast<char*>(vals);
     char* m = reinterpret_cast<char*>(meta);
     const uint32_t nb = (uint32_t)nblk;
-    if (es == 2) hipLaunchKernelGGL((prune_compress_kblock_kernel<2, false>), grid, block, 0, stream, a, v, m, M, K, nb);
-    else if (is_int) hipLaunchKernelGGL((prune_compress_kblock_kernel<1, true>), grid, block, 0, stream, a, v, m, M, K, nb);
-    else hipLaunchKernelGGL((prune_compress_kblock_kernel<1, false>), grid, block, 0, stream, a, v, m, M, K, nb);
+    if (es == 2 && nb_per_wg == 4)
+      hipLaunchKernelGGL((prune_compress_kblock_kernel<2, false, 4>), grid, block, 0, stream, a, v, m, M, K, nb);
+    else if (es == 2)
+      hipLaunchKernelGGL((prune_compress_kblock_kernel<2, false, 1>), grid, block, 0, stream, a, v, m, M, K, nb);
+    else if (is_int)
+      hipLaunchKernelGGL((prune_compress_kblock_kernel<1, true, 1>), grid, block, 0, stream, a, v, m, M, K, nb);
+    else
+      hipLaunchKernelGGL((prune_compress_kblock_kernel<1, false, 1>), grid, block, 0, stream, a, v, m, M, K, nb);
     return hipGetLastError();
   }
   const int64_t nchunks = M * K * es / 16;
