@@ -563,35 +563,31 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
 // loads past the wave's last step read nothing, so every step issues the
 // same number of loads.  The 8 partial tiles are summed on chip in a fixed
 // order (deterministic).
-//   D = 4 when the B slice is at most 2 KiB (N <= 16), else 2 (N <= 64).
+//   D = 5 when the B slice is at most 2 KiB (N <= 16), else 2 (N <= 64).
+//   (bf16 4096 x 16 x 4096 back to back: D = 5 8.19 us, 4 8.53 us, 6 9.19 us;
+//   inside the bench step 5 and 4 measure the same.)
 // ----------------------------------------------------------------------------
 constexpr int kSmallWaves = 8;
 constexpr int kSmallA = 1024, kSmallM = 256;
 
 template <int D>
-__host__ __device__ constexpr int small_bslice() { return D == 4 ? 2048 : 8192; }
+__host__ __device__ constexpr int small_bslice() { return D == 2 ? 8192 : 2048; }
 template <int D>
 __host__ __device__ constexpr int small_slot() { return kSmallA + kSmallM + small_bslice<D>(); }
 
-// s_waitcnt vmcnt(n) for a run-time n <= 15.
-__device__ __forceinline__ void wait_vm_upto15(int n) {
+// s_waitcnt vmcnt(n) for a run-time n <= 31 (larger n waits for 31).
+__device__ __forceinline__ void wait_vm_upto31(int n) {
   switch (n) {
-    case 0: waitcnt<0>(); break;
-    case 1: waitcnt<1>(); break;
-    case 2: waitcnt<2>(); break;
-    case 3: waitcnt<3>(); break;
-    case 4: waitcnt<4>(); break;
-    case 5: waitcnt<5>(); break;
-    case 6: waitcnt<6>(); break;
-    case 7: waitcnt<7>(); break;
-    case 8: waitcnt<8>(); break;
-    case 9: waitcnt<9>(); break;
-    case 10: waitcnt<10>(); break;
-    case 11: waitcnt<11>(); break;
-    case 12: waitcnt<12>(); break;
-    case 13: waitcnt<13>(); break;
-    case 14: waitcnt<14>(); break;
-    default: waitcnt<15>(); break;
+#define SP24_WAIT_CASE(i) \
+  case i: waitcnt<i>(); break;
+    SP24_WAIT_CASE(0) SP24_WAIT_CASE(1) SP24_WAIT_CASE(2) SP24_WAIT_CASE(3) SP24_WAIT_CASE(4) SP24_WAIT_CASE(5)
+    SP24_WAIT_CASE(6) SP24_WAIT_CASE(7) SP24_WAIT_CASE(8) SP24_WAIT_CASE(9) SP24_WAIT_CASE(10) SP24_WAIT_CASE(11)
+    SP24_WAIT_CASE(12) SP24_WAIT_CASE(13) SP24_WAIT_CASE(14) SP24_WAIT_CASE(15) SP24_WAIT_CASE(16) SP24_WAIT_CASE(17)
+    SP24_WAIT_CASE(18) SP24_WAIT_CASE(19) SP24_WAIT_CASE(20) SP24_WAIT_CASE(21) SP24_WAIT_CASE(22) SP24_WAIT_CASE(23)
+    SP24_WAIT_CASE(24) SP24_WAIT_CASE(25) SP24_WAIT_CASE(26) SP24_WAIT_CASE(27) SP24_WAIT_CASE(28) SP24_WAIT_CASE(29)
+    SP24_WAIT_CASE(30)
+#undef SP24_WAIT_CASE
+    default: waitcnt<31>(); break;
   }
 }
 
@@ -765,7 +761,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
     for (int u = 0; u < D; ++u) {
       if (j + u >= nw) break;
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm_upto15((D - 1) * LPS);  // local step j+u has landed (the D-1 later ones may still be in flight)
+      wait_vm_upto31((D - 1) * LPS);  // local step j+u has landed (the D-1 later ones may still be in flight)
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       compute(u);
@@ -836,8 +832,8 @@ static hipError_t launch_op(const void* A_vals, const uint32_t* meta, const void
   }
   if (N <= 64) {
     const dim3 grid((unsigned)((M + 15) / 16)), block(kSmallWaves * 64);
-    if ((int64_t)op_kstep(OP) * N * op_esize(OP) <= small_bslice<4>())
-      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 4, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep);
+    if ((int64_t)op_kstep(OP) * N * op_esize(OP) <= small_bslice<5>())
+      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 5, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep);
     else
       hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 2, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep);
     return hipGetLastError();
