@@ -445,33 +445,35 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
     for (int g = 0; g < 8; ++g) read_group(cur, g);
   };
   // Matrix phase: the 32 MFMAs of the fragments in registers, one load
-  // instruction of the step described by `d` after each group of four.
+  // instruction of the step described by `d` after each group of four.  The
+  // MFMAs go B-major (each B fragment against the 8 A row tiles, in two
+  // groups of four): 1.5 % faster than A-major, the same bits.
   auto mfma_phase = [&](const DmaStep& d) {
 #pragma unroll
-    for (int tm = 0; tm < 8; ++tm) {
-      if constexpr (LAYOUT == SP24_LAYOUT_ROW) {
+    for (int q = 0; q < 8; ++q) {
+      const int tn = q >> 1;
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = smfmac16<OP>(acc[tm][tn], f.a[tm], f.b[tn], f.idx[tm]);
-      } else if constexpr (ES == 2) {  // word tm sits in half tm%2 of register tm/2
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
+      for (int h = 0; h < 4; ++h) {
+        const int tm = 4 * (q & 1) + h;
+        if constexpr (LAYOUT == SP24_LAYOUT_ROW) {
+          acc[tm][tn] = smfmac16<OP>(acc[tm][tn], f.a[tm], f.b[tn], f.idx[tm]);
+        } else if constexpr (ES == 2) {  // word tm sits in half tm%2 of register tm/2
           if (tm & 1) acc[tm][tn] = smfmac16<OP, 1>(acc[tm][tn], f.a[tm], f.b[tn], f.idxv[0][tm >> 1]);
           else acc[tm][tn] = smfmac16<OP, 0>(acc[tm][tn], f.a[tm], f.b[tn], f.idxv[0][tm >> 1]);
+        } else {
+          acc[tm][tn] = smfmac16<OP>(acc[tm][tn], f.a[tm], f.b[tn], f.idxv[tm >> 2][tm & 3]);
         }
-      } else {
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = smfmac16<OP>(acc[tm][tn], f.a[tm], f.b[tn], f.idxv[tm >> 2][tm & 3]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (tm == 0) dma_piece<OP, LAYOUT, BL, 0>(d, w);
-      if (tm == 1) dma_piece<OP, LAYOUT, BL, 2>(d, w);
-      if (tm == 2) dma_piece<OP, LAYOUT, BL, 3>(d, w);
-      if (tm == 3) dma_piece<OP, LAYOUT, BL, 1>(d, w);
-      if (tm == 4) dma_piece<OP, LAYOUT, BL, 4>(d, w);
-      if (tm == 5) dma_piece<OP, LAYOUT, BL, 5>(d, w);
-      if (tm == 6) dma_piece<OP, LAYOUT, BL, 6>(d, w);
+      if (q == 0) dma_piece<OP, LAYOUT, BL, 0>(d, w);
+      if (q == 1) dma_piece<OP, LAYOUT, BL, 2>(d, w);
+      if (q == 2) dma_piece<OP, LAYOUT, BL, 3>(d, w);
+      if (q == 3) dma_piece<OP, LAYOUT, BL, 1>(d, w);
+      if (q == 4) dma_piece<OP, LAYOUT, BL, 4>(d, w);
+      if (q == 5) dma_piece<OP, LAYOUT, BL, 5>(d, w);
+      if (q == 6) dma_piece<OP, LAYOUT, BL, 6>(d, w);
       if constexpr (L == 8)
-        if (tm == 7) dma_piece<OP, LAYOUT, BL, 7>(d, w);
+        if (q == 7) dma_piece<OP, LAYOUT, BL, 7>(d, w);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
