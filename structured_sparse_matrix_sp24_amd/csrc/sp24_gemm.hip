@@ -29,7 +29,6 @@
 // (N x K, sp24_b_layout SP24_B_NK) one k-step of a column is 128 contiguous
 // bytes, both runs are 16-byte chunks of it (chunks gb and gb+4), and two
 // plain 16-byte LDS reads fetch a fragment.
-#include <type_traits>
 
 #include "sp24_internal.hpp"
 

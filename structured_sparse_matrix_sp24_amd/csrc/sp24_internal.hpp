@@ -65,27 +65,13 @@ __device__ __forceinline__ i32x4 smfmac16(i32x4 acc, i32x4 a, i32x8 b, int idx) 
 static constexpr uint32_t kOOB = 0x7FFFFFF0u;          // offset used for masked lanes
 static constexpr uint64_t kMaxRecords = 0x7FFFFF00ull;  // keep every range below kOOB
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
-  uint32_t n = (uint32_t)(bytes < kMaxRecords ? bytes : kMaxRecords);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, SP24_RSRC_WORD3);
-}
-
-// 16 bytes per lane from global memory straight into LDS.  The LDS address is
-// lds_base + 16 * lane (wave-uniform base).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, SP24_LDS void* lds_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, (int)voff, 0, 0, 0);
-}
-// 4 bytes per lane; LDS address lds_base + 4 * lane.
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, SP24_LDS void* lds_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 4, (int)voff, 0, 0, 0);
-}
-
-// The same direct-to-LDS loads issued through inline assembly.  The compiler
+// Direct-to-LDS buffer loads, issued through inline assembly.  The compiler
 // then does not see an LDS write, so it inserts no waits of its own for them
-// (its alias tracking for these loads is lost across branches and the loop
-// back-edge, which made it wait for every freshly issued load); callers wait
-// with explicit s_waitcnt vmcnt and order LDS reads with barriers that carry
-// a memory clobber.  The buffer resource is a plain SGPR quad.
+// (with the compiler-visible builtin, its alias tracking for these loads was
+// lost across branches and the loop back-edge, which made it wait for every
+// freshly issued load); callers wait with explicit s_waitcnt vmcnt and order
+// LDS reads with barriers that carry a memory clobber.  The buffer resource
+// is a plain SGPR quad; the LDS address is m0 + the lane's 16 (or 4) bytes.
 __device__ __forceinline__ i32x4 make_rsrc4(const void* base, uint64_t bytes) {
   const uint64_t b = (uint64_t)base;
   const uint32_t n = (uint32_t)(bytes < kMaxRecords ? bytes : kMaxRecords);
@@ -176,14 +162,6 @@ __device__ __forceinline__ void store_out1(void* C, int64_t o, int col, float v,
       *p = (__bf16)d;
     }
   }
-}
-
-// A copy of v the compiler cannot see through.  Addresses derived from it are
-// recomputed where they are used (a few VALU ops that co-issue with MFMA)
-// instead of being hoisted out of the K loop and held in registers.
-__device__ __forceinline__ int opaque(int v) {
-  asm volatile("" : "+v"(v));
-  return v;
 }
 
 }  // namespace sp24
