@@ -88,9 +88,7 @@ constexpr int kLdsStage = kLdsA + kLdsB + kLdsM;  // 52 KiB; three stages = 156 
 // bytes 1024t .. +1024, and the 16 bytes fragment lane l needs (row l%16,
 // chunk l/16) sit at 16l, so each fragment is one contiguous read.  (Stored
 // row-major with an XOR swizzle, the same reads measured about 60% of the
-// LDS read rate of contiguous ones on gfx950.)  The small-N kernel stores its
-// A rows row-major with chunk c of row r at chunk c ^ swzA(r).
-__device__ __forceinline__ int swzA(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
+// LDS read rate of contiguous ones on gfx950.)
 // B tile, 16-bit: row k holds 256 columns = 16 pairs of chunks; pair p stored
 // at p ^ swzB16(k).  8-bit: 16 chunks per row; chunk c stored at c ^ swzB8(k).
 // For the rows one transpose read touches these depend only on the lane, so
@@ -555,41 +553,29 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
 // ----------------------------------------------------------------------------
 // Small-N kernel (N <= 64): bound by HBM (A is read once, B is small and stays
 // in L2).  A workgroup of 8 waves owns one 16-row tile and all N columns; the
-// waves take the k-steps round-robin (wave w: steps w, w+8, ...).  Each wave
-// keeps D of its steps in flight in its own LDS ring: a slot holds the step's
-// A values (16 rows x 64 B, chunk-swizzled), the 16 rows' idx words (256 B)
-// and the B slice (KS rows x N; for B stored N x K, N rows of the step's 128
-// bytes with chunk c of row n at c ^ swzBT(n)).  All three arrive by direct-to-LDS loads,
-// issued through inline assembly and waited for with explicit vmcnt counts;
-// loads past the wave's last step read nothing, so every step issues the
-// same number of loads.  The 8 partial tiles are summed on chip in a fixed
-// order (deterministic).
-//   D = 5 when the B slice is at most 2 KiB (N <= 16), else 2 (N <= 64).
-//   (bf16 4096 x 16 x 4096 back to back: D = 5 8.19 us, 4 8.53 us, 6 9.19 us;
-//   inside the bench step 5 and 4 measure the same.)
+// waves take the k-steps round-robin (wave w: steps w, w+8, ...).  A wave
+// works through its steps in chunks of D, all of whose loads are in flight at
+// once: the B slices (KS rows x N; for B stored N x K, N rows of the step's
+// 128 bytes with chunk c of row n at c ^ swzBT(n)) go into the wave's LDS
+// ring by direct-to-LDS loads issued through inline assembly, then the A
+// fragments (16 bytes per lane) and idx words (4 bytes) straight into
+// registers.  Loads past the wave's last step read nothing, so every step
+// issues the same number of loads.  The 8 partial tiles are summed on chip
+// in a fixed order (deterministic).
+//   D = 16 KiB / B-slice bytes: 8 (N <= 16), 4 (N <= 32), 2 (N <= 64), so
+//   the ring holds 128 KiB of B per workgroup.  (bf16 4096 x 16 x 4096:
+//   with A and idx staged in LDS as well the ring could hold only 5 steps,
+//   7.6 us per launch.)
 // ----------------------------------------------------------------------------
 constexpr int kSmallWaves = 8;
-constexpr int kSmallA = 1024, kSmallM = 256;
+constexpr int kSmallRingBytes = 16384;  // per wave
 
 template <int D>
-__host__ __device__ constexpr int small_bslice() { return D == 2 ? 8192 : 2048; }
-template <int D>
-__host__ __device__ constexpr int small_slot() { return kSmallA + kSmallM + small_bslice<D>(); }
+__host__ __device__ constexpr int small_bslice() { return kSmallRingBytes / D; }
 
-// s_waitcnt vmcnt(n) for a run-time n <= 31 (larger n waits for 31).
-__device__ __forceinline__ void wait_vm_upto31(int n) {
-  switch (n) {
-#define SP24_WAIT_CASE(i) \
-  case i: waitcnt<i>(); break;
-    SP24_WAIT_CASE(0) SP24_WAIT_CASE(1) SP24_WAIT_CASE(2) SP24_WAIT_CASE(3) SP24_WAIT_CASE(4) SP24_WAIT_CASE(5)
-    SP24_WAIT_CASE(6) SP24_WAIT_CASE(7) SP24_WAIT_CASE(8) SP24_WAIT_CASE(9) SP24_WAIT_CASE(10) SP24_WAIT_CASE(11)
-    SP24_WAIT_CASE(12) SP24_WAIT_CASE(13) SP24_WAIT_CASE(14) SP24_WAIT_CASE(15) SP24_WAIT_CASE(16) SP24_WAIT_CASE(17)
-    SP24_WAIT_CASE(18) SP24_WAIT_CASE(19) SP24_WAIT_CASE(20) SP24_WAIT_CASE(21) SP24_WAIT_CASE(22) SP24_WAIT_CASE(23)
-    SP24_WAIT_CASE(24) SP24_WAIT_CASE(25) SP24_WAIT_CASE(26) SP24_WAIT_CASE(27) SP24_WAIT_CASE(28) SP24_WAIT_CASE(29)
-    SP24_WAIT_CASE(30)
-#undef SP24_WAIT_CASE
-    default: waitcnt<31>(); break;
-  }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = (uint32_t)(bytes < kMaxRecords ? bytes : kMaxRecords);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, SP24_RSRC_WORD3);
 }
 
 template <int OP, int LAYOUT, int D, int BL>
@@ -598,8 +584,9 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
                                                                         const char* __restrict__ B, void* C, int M,
                                                                         int N, int K, Epilogue ep) {
   constexpr int KS = op_kstep(OP), ES = op_esize(OP), MB = meta_step_bytes<OP>();
-  constexpr int SLOT = small_slot<D>();
-  __shared__ __attribute__((aligned(1024))) char lB[kSmallWaves * D * SLOT];
+  constexpr int SLOT = small_bslice<D>();
+  constexpr int NT = 8 / D;  // column tiles computed: the slice of D = 8, 4, 2 holds N <= 16, 32, 64
+  __shared__ __attribute__((aligned(1024))) char lB[kSmallWaves * kSmallRingBytes];
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), l = lane_id();
   // Workgroups are dispatched round-robin over the 8 XCDs.  In the K-blocked
   // layout the metadata of the 8 row tiles of a 128-row group is interleaved
@@ -620,27 +607,23 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
   const int64_t ldbk = (int64_t)K * ES;                // bytes per N x K row
   const int chunks_per_row = ldb >> 4;
   const int slice_instr = (KS * ldb) >> 10;            // 1 KiB per load (KS*ldb = 128*N is a multiple of 1 KiB)
-  const int LPS = 2 + slice_instr;                     // loads per step
   const int64_t btotal = (int64_t)K * ldb;
   const int t16 = (m0 & 127) >> 4;                     // KBLOCK: row tile of the tile inside its 128-row group
-  SP24_LDS char* ring = (SP24_LDS char*)lB + w * D * SLOT;
+  SP24_LDS char* ring = (SP24_LDS char*)lB + w * kSmallRingBytes;
 
   // Per-lane load offsets, computed once (the loop only adds scalar step
-  // offsets).  A: lane l -> row l/4, chunk (l%4) ^ swzA(row).  idx: lane
-  // l = (row r = l/4, word g = l%4) -> the dword holding word g of row m0+r
-  // (K-blocked: inside the tile's 128-row group, for row tile t16; row-major:
-  // for 16-bit types the dword holding the u16 word g).  B: 1 KiB per load,
-  // lane l of load q -> chunk 64q + l of the slice (N x K: row n = 8q + l/8,
-  // chunk (l%8) ^ swzBT(n) of the step).
-  const int a_row = l >> 2, a_ch = (l & 3) ^ swzA(l >> 2);
-  const int m_r = l >> 2, m_g = l & 3;
-  const uint32_t offA = LAYOUT == SP24_LAYOUT_KBLOCK ? (uint32_t)(a_row * 64 + 16 * a_ch)
-                                                     : (uint32_t)(a_row * rowA + 16 * a_ch);
+  // offsets).  A: lane l -> row s = l%16, chunk ga = l/16 (the MFMA's own
+  // fragment).  idx: the dword holding word ga of row m0+s (K-blocked: inside
+  // the tile's 128-row group, for row tile t16; row-major: for 16-bit types
+  // the dword holding the u16 word ga).  B: 1 KiB per load, lane l of load q
+  // -> chunk 64q + l of the slice (N x K: row n = 8q + l/8, chunk
+  // (l%8) ^ swzBT(n) of the step).
+  const uint32_t offA = LAYOUT == SP24_LAYOUT_KBLOCK ? (uint32_t)(s * 64 + 16 * ga) : (uint32_t)(s * rowA + 16 * ga);
   uint32_t offM;
   if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK)
-    offM = ES == 2 ? (uint32_t)(((m_r * 4 + m_g) * 4 + (t16 >> 1)) * 4) : (uint32_t)(((m_r * 4 + m_g) * 8 + t16) * 4);
+    offM = ES == 2 ? (uint32_t)(((s * 4 + ga) * 4 + (t16 >> 1)) * 4) : (uint32_t)(((s * 4 + ga) * 8 + t16) * 4);
   else
-    offM = (uint32_t)(m_r * rowM + (ES == 2 ? 4 * (m_g >> 1) : 4 * m_g));
+    offM = (uint32_t)(s * rowM + (ES == 2 ? 4 * (ga >> 1) : 4 * ga));
   uint32_t offB[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -654,8 +637,8 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
     }
   }
   const int nfull = K / KS;
-  const i32x4 raRow = make_rsrc4(A_vals + (int64_t)m0 * rowA, (uint64_t)(M - m0) * rowA);
-  const i32x4 rmRow = make_rsrc4(meta + (int64_t)m0 * rowM, (uint64_t)(M - m0) * rowM);
+  const __amdgpu_buffer_rsrc_t raRow = buffer_rsrc(A_vals + (int64_t)m0 * rowA, (uint64_t)(M - m0) * rowA);
+  const __amdgpu_buffer_rsrc_t rmRow = buffer_rsrc(meta + (int64_t)m0 * rowM, (uint64_t)(M - m0) * rowM);
 
   // Every workgroup reads all of B; so that the workgroups in flight do not
   // all ask for the same few B lines at once, each one starts its waves'
@@ -663,35 +646,18 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
   // summation order, and so the result, does not depend on timing).
   const int rot = nw > 0 ? (int)(blockIdx.x % (unsigned)nw) : 0;
 
-  // Loads of this wave's local step j (global step w + 8*((j + rot) % nw))
-  // into ring slot u.  Local steps past nw get empty buffer ranges (nothing
-  // is read); in the step that ends past K the lanes past the row end are
-  // masked.
-  auto issue = [&](int j, int u) {
+  // Global k-step of this wave's local step j (local steps past nw map to
+  // steps past the end, whose loads read nothing).
+  auto kstep = [&](int j) {
     const bool in = j < nw;
     const int jr = j + rot >= nw ? j + rot - nw : j + rot;
-    const int ks = w + kSmallWaves * (in ? jr : j);
+    return w + kSmallWaves * (in ? jr : j);
+  };
+  // The B slice of local step j into ring slot u (direct-to-LDS loads).
+  auto issue_b = [&](int j, int u) {
+    const bool in = j < nw;
+    const int ks = kstep(j);
     const uint32_t la = lds_addr(ring + u * SLOT);
-    uint32_t oa, om;
-    i32x4 ra, rm;
-    if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK) {
-      ra = make_rsrc4(A_vals + ((int64_t)ks * M + m0) * 64, in ? (uint64_t)(M - m0) * 64 : 0u);
-      rm = make_rsrc4(meta + ((int64_t)ks * Mp + (m0 & ~127)) * MB, in ? (uint64_t)128 * MB : 0u);
-      oa = offA;
-      om = offM;
-    } else {
-      ra = raRow;
-      rm = rmRow;
-      oa = in ? offA + (uint32_t)(ks * 64) : kOOB;
-      om = in ? offM + (uint32_t)(ks * MB) : kOOB;
-    }
-    if (ks >= nfull && in) {  // the partial last step: mask what lies past K
-      if (16 * a_ch >= rowA - (int64_t)ks * 64) oa = kOOB;
-      if constexpr (LAYOUT == SP24_LAYOUT_ROW)
-        if ((int64_t)ks * MB + (ES == 2 ? 4 * (m_g >> 1) : 4 * m_g) >= rowM) om = kOOB;
-    }
-    dma16_asm(ra, la, oa, 0u);
-    dma4_asm(rm, la + kSmallA, om, 0u);
     if constexpr (BL == SP24_B_NK) {
       // bytes ks*128 on of every row; the end of the row in the last step is
       // masked per lane
@@ -703,7 +669,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
         if (q < slice_instr) {
           uint32_t ob = offB[q];
           if (tail && 16 * ((l & 7) ^ swzBT(8 * q + (l >> 3))) >= valid) ob = kOOB;
-          dma16_asm(rb, la + kSmallA + kSmallM + q * 1024, ob, 0u);
+          dma16_asm(rb, la + q * 1024, ob, 0u);
         }
       }
     } else {
@@ -711,23 +677,50 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
       const i32x4 rb = make_rsrc4(B + start, (in && start < btotal) ? (uint64_t)(btotal - start) : 0u);
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        if (q < slice_instr) dma16_asm(rb, la + kSmallA + kSmallM + q * 1024, offB[q], 0u);
+        if (q < slice_instr) dma16_asm(rb, la + q * 1024, offB[q], 0u);
     }
   };
+  // The A fragment and idx word of local step j, into registers.  In the
+  // step that ends past K the lanes past the row end are masked.
+  auto load_a = [&](int j, i32x4& a_out, int& idx_out) {
+    const bool in = j < nw;
+    const int ks = kstep(j);
+    uint32_t oa, om;
+    __amdgpu_buffer_rsrc_t ra, rm;
+    if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK) {
+      ra = buffer_rsrc(A_vals + ((int64_t)ks * M + m0) * 64, in ? (uint64_t)(M - m0) * 64 : 0u);
+      rm = buffer_rsrc(meta + ((int64_t)ks * Mp + (m0 & ~127)) * MB, in ? (uint64_t)128 * MB : 0u);
+      oa = offA;
+      om = offM;
+    } else {
+      ra = raRow;
+      rm = rmRow;
+      oa = in ? offA + (uint32_t)(ks * 64) : kOOB;
+      om = in ? offM + (uint32_t)(ks * MB) : kOOB;
+    }
+    if (ks >= nfull && in) {
+      if (16 * ga >= rowA - (int64_t)ks * 64) oa = kOOB;
+      if constexpr (LAYOUT == SP24_LAYOUT_ROW)
+        if ((int64_t)ks * MB + (ES == 2 ? 4 * (ga >> 1) : 4 * ga) >= rowM) om = kOOB;
+    }
+    a_out = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)oa, 0, 0));
+    idx_out = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, (int)om, 0, 0);
+  };
 
-  i32x4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-  // One step from ring slot u.
-  auto compute = [&](int u) {
-    const SP24_LDS char* slot = ring + u * SLOT;
-    const i32x4 a = *(const SP24_LDS i32x4*)(slot + s * 64 + 16 * (ga ^ swzA(s)));
-    int idx = *(const SP24_LDS int*)(slot + kSmallA + 4 * (s * 4 + ga));
-    if constexpr (LAYOUT == SP24_LAYOUT_ROW && ES == 2) idx = (int)((uint32_t)idx >> (16 * (ga & 1)));
-    const SP24_LDS char* sb = slot + kSmallA + kSmallM;
-    // (unrolled with a guard: a run-time index into the accumulators would
-    // turn into indirect register addressing)
+  i32x4 acc[NT];
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
-      if (tn >= nt) break;
+  for (int tn = 0; tn < NT; ++tn) acc[tn] = i32x4{0, 0, 0, 0};
+  // One step from ring slot u.
+  auto compute = [&](int u, const i32x4 a, int idx) {
+    if constexpr (LAYOUT == SP24_LAYOUT_ROW && ES == 2) idx = (int)((uint32_t)idx >> (16 * (ga & 1)));
+    const SP24_LDS char* sb = ring + u * SLOT;
+    // K-blocked 16-bit idx: the tile's word sits in half t16%2 of the dword
+    if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK && ES == 2) idx = (int)((uint32_t)idx >> (16 * (t16 & 1)));
+    // All NT column tiles, also those past N (their B is other columns' data
+    // or zeros, and their results are not stored): no branches, so the
+    // compiler keeps the loads in issue order.
+#pragma unroll
+    for (int tn = 0; tn < NT; ++tn) {
       i32x8 b;
       if constexpr (BL == SP24_B_NK) {
         const int n = tn * 16 + s;
@@ -749,39 +742,47 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
       }
       b = i32x8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
       }
-      // K-blocked 16-bit idx: the tile's word sits in half t16%2 of the dword
-      if (LAYOUT == SP24_LAYOUT_KBLOCK && ES == 2 && (t16 & 1)) acc[tn] = smfmac16<OP, 1>(acc[tn], a, b, idx);
-      else acc[tn] = smfmac16<OP, 0>(acc[tn], a, b, idx);
+      acc[tn] = smfmac16<OP, 0>(acc[tn], a, b, idx);
     }
   };
 
+  // Chunks of D local steps: all B slices first (direct-to-LDS), then all A
+  // fragments and idx words (register loads the compiler sees and waits for
+  // itself, exactly, since nothing it cannot see is issued after them).
+  // Loads complete in order, so vmcnt(2D) means every B slice of the chunk
+  // has landed.
+  for (int j0 = 0; j0 < nw; j0 += D) {
+    i32x4 ar[D];
+    int ir[D];
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int u = 0; u < D; ++u) issue(u, u);
-  for (int j = 0; j < nw; j += D) {
+    for (int u = 0; u < D; ++u) issue_b(j0 + u, u);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      if (j + u >= nw) break;
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vm_upto31((D - 1) * LPS);  // local step j+u has landed (the D-1 later ones may still be in flight)
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      compute(u);
-      waitcnt<63, 0>();  // this slot's reads are done before it is refilled
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      issue(j + u + D, u);
-    }
+    for (int u = 0; u < D; ++u) load_a(j0 + u, ar[u], ir[u]);
+    __builtin_amdgcn_sched_barrier(0);
+    waitcnt<2 * D>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // (every slot, also past the wave's last step: those read nothing, their
+    // A and B are zero and add nothing; a guard here would let the compiler
+    // sink the register loads into it, after the waits)
+#pragma unroll
+    for (int u = 0; u < D; ++u) compute(u, ar[u], ir[u]);
+    waitcnt<63, 0>();  // the slots' reads are done before the next chunk refills them
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
   }
   // ---- reduce the 8 partial tiles in LDS (fixed order), then epilogue
   waitcnt<0, 0>();
   __syncthreads();
   int* red = (int*)&lB[0];  // 8 waves x 4 tiles x 64 lanes x 4 regs x 4 B = 32 KiB
 #pragma unroll
-  for (int tn = 0; tn < 4; ++tn) {
-    if (tn >= nt) break;
+  for (int tn = 0; tn < NT; ++tn)
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[((w * 4 + tn) * 4 + r) * 64 + l] = acc[tn][r];
-  }
   __syncthreads();
   for (int e = threadIdx.x; e < 16 * nt * 16; e += kSmallWaves * 64) {
     const int tn = e >> 8, within = e & 255;
@@ -833,8 +834,11 @@ static hipError_t launch_op(const void* A_vals, const uint32_t* meta, const void
   }
   if (N <= 64) {
     const dim3 grid((unsigned)((M + 15) / 16)), block(kSmallWaves * 64);
-    if ((int64_t)op_kstep(OP) * N * op_esize(OP) <= small_bslice<5>())
-      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 5, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep);
+    const int64_t slice = (int64_t)op_kstep(OP) * N * op_esize(OP);  // B bytes per k-step
+    if (slice <= small_bslice<8>())
+      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 8, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep);
+    else if (slice <= small_bslice<4>())
+      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 4, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep);
     else
       hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 2, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep);
     return hipGetLastError();
