@@ -202,6 +202,23 @@ def test_gemm_random_b_transposed(pkg, a_type, b_type, M, N, K, layout):
     check_gemm_full(pkg, vals, meta, a_type, c.B, b_type, layout=layout, b_layout=NK)
 
 
+# Small-N chunks: each wave takes every 8th k-step and works through them in
+# chunks of 8, 4 or 2 (N <= 16, 32, 64).  K is chosen so that waves get more
+# than one chunk, a partial last chunk, different step counts, and a partial
+# last k-step (the K tail).
+@pytest.mark.parametrize("b_layout", [KN, NK])
+@pytest.mark.parametrize("a_type,b_type", [(wl.BF16, wl.BF16), (wl.I8, wl.I8), (wl.E4M3, wl.E5M2)])
+@pytest.mark.parametrize("N,steps_extra", [(16, 0), (16, 19), (32, 5), (48, 3), (64, 1)])
+def test_gemm_small_n_chunks(pkg, a_type, b_type, N, steps_extra, b_layout):
+    ks = 64 if wl.ESIZE[a_type] == 2 else 128
+    K = ks * (8 * 8 + steps_extra) + 32      # 8 full chunks' worth for D = 8, extra steps, a 32-wide tail
+    M = 128 if N == 16 else 40               # 8 row tiles (the XCD-grouped tile order) or a ragged 2.5
+    _say(f"gemm small-N chunks a={a_type} M={M} N={N} K={K} b_layout={b_layout}")
+    c = wl.random_case(41, M, N, K, a_type, b_type)
+    vals, meta = oracle.prune_compress(c.A, a_type)
+    check_gemm_full(pkg, vals, meta, a_type, c.B, b_type, b_layout=b_layout)
+
+
 @pytest.mark.parametrize("a_type,b_type", [(wl.F16, wl.F16), (wl.I8, wl.I8), (wl.E5M2, wl.E4M3)])
 @pytest.mark.parametrize("N", [16, 48, 512])
 def test_b_layouts_give_identical_bits(pkg, a_type, b_type, N):
