@@ -27,53 +27,94 @@
 
 namespace sp24 {
 
-// Keep mask of one group of 4 magnitude keys: bit i set iff element i is among
-// the two largest keys, ties going to the lower index.  rank_i counts the
-// elements that beat i; i is kept iff rank_i < 2 (the ranks are a permutation
-// of 0..3, so exactly two bits are set).
-__device__ __forceinline__ uint32_t keep_mask(uint32_t k0, uint32_t k1, uint32_t k2, uint32_t k3) {
-  const uint32_t b01 = k1 > k0, b02 = k2 > k0, b03 = k3 > k0;
-  const uint32_t b12 = k2 > k1, b13 = k3 > k1, b23 = k3 > k2;
-  const uint32_t r0 = b01 + b02 + b03;
-  const uint32_t r1 = (1u - b01) + b12 + b13;
-  const uint32_t r2 = (1u - b02) + (1u - b12) + b23;
-  const uint32_t r3 = (1u - b03) + (1u - b13) + (1u - b23);
-  return (uint32_t)(r0 < 2) | ((uint32_t)(r1 < 2) << 1) | ((uint32_t)(r2 < 2) << 2) | ((uint32_t)(r3 < 2) << 3);
+// Median of three (the compiler forms max3 from max(max()) itself, but not
+// the median).
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
-// One group of four 16-bit values packed in a 64-bit word (element p in bits
-// 16p..16p+15).  Returns the two kept values (low half = lower position) and
-// writes the 4-bit code p0 | p1 << 2.
-__device__ __forceinline__ uint32_t group16(uint64_t w, uint32_t& nib) {
-  const uint32_t e0 = (uint32_t)w & 0xFFFFu, e1 = (uint32_t)(w >> 16) & 0xFFFFu;
-  const uint32_t e2 = (uint32_t)(w >> 32) & 0xFFFFu, e3 = (uint32_t)(w >> 48) & 0xFFFFu;
-  const uint32_t m = keep_mask(e0 & 0x7FFFu, e1 & 0x7FFFu, e2 & 0x7FFFu, e3 & 0x7FFFu);
-  const uint32_t p0 = __builtin_ctz(m), p1 = 31u - __builtin_clz(m);
-  nib = p0 | (p1 << 2);
-  const uint32_t v0 = (uint32_t)(w >> (16 * p0)) & 0xFFFFu;
-  const uint32_t v1 = (uint32_t)(w >> (16 * p1)) & 0xFFFFu;
-  return v0 | (v1 << 16);
+// Top two of one group of four.  Each element gets a tagged key: its
+// magnitude key shifted up by one byte, with 3 - position in the low byte.
+// The tagged keys are distinct, a larger magnitude ranks higher, and between
+// equal magnitudes the lower position ranks higher, so the two largest tagged
+// keys are the two elements kept.  They are found with a three-input maximum
+// and median of the first three and one compare-exchange with the fourth:
+//   first  = max(max3(t0, t1, t2), t3)
+//   second = max(med3(t0, t1, t2), min(max3(t0, t1, t2), t3)).
+// Returns the tags of the two kept elements as hi = larger tag (lower
+// position p0 = 3 - hi) and lo (p1 = 3 - lo).  About 25 vector instructions
+// per group with the key and value byte permutes below, against about 70 for
+// pairwise rank counting, which left the 8-bit kernels bound by the ALU.
+__device__ __forceinline__ void top2_tags(uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3, uint32_t& hi,
+                                          uint32_t& lo) {
+  const uint32_t m3 = max(max(t0, t1), t2), d3 = med3_u32(t0, t1, t2);
+  const uint32_t first = max(m3, t3), second = max(d3, min(m3, t3));
+  const uint32_t ta = first & 3u, tb = second & 3u;
+  hi = max(ta, tb);
+  lo = min(ta, tb);
+}
+// 4-bit code p0 | p1 << 2 of a group from its kept tags.
+__device__ __forceinline__ uint32_t code_of(uint32_t hi, uint32_t lo) { return 15u - (hi + (lo << 2)); }
+
+// Byte permutes build the tagged keys: the key's bytes move up by one and
+// byte 0 takes the tag 3 - p from the constant word below (its byte p is
+// 3 - p); selector 12 gives a zero byte.
+constexpr uint32_t kTagBytes = 0x00010203u;
+
+// One group of four 16-bit values in two words (element p in bits
+// 16(p%2).. of word p/2).  Returns the two kept values (low half = lower
+// position) and writes the 4-bit code.  The values are picked with a byte
+// permute: selector bytes 2p0, 2p0+1, 2p1, 2p1+1 of the 8 bytes lo:hi.
+__device__ __forceinline__ uint32_t group16(uint32_t lo_w, uint32_t hi_w, uint32_t& nib) {
+  const uint32_t a = lo_w & 0x7FFF7FFFu, b = hi_w & 0x7FFF7FFFu;  // magnitude keys
+  const uint32_t t0 = __builtin_amdgcn_perm(kTagBytes, a, 0x0C010004u);
+  const uint32_t t1 = __builtin_amdgcn_perm(kTagBytes, a, 0x0C030205u);
+  const uint32_t t2 = __builtin_amdgcn_perm(kTagBytes, b, 0x0C010006u);
+  const uint32_t t3 = __builtin_amdgcn_perm(kTagBytes, b, 0x0C030207u);
+  uint32_t hi, lo;
+  top2_tags(t0, t1, t2, t3, hi, lo);
+  nib = code_of(hi, lo);
+  // p0 = 3 - hi, p1 = 3 - lo: selector 0x01000100 + p0*0x0202 + p1*0x02020000
+  // (each 16-bit half of hi | lo << 16 is at most 3, so one 24-bit multiply
+  // by 0x0202 doubles and copies both into their two selector bytes)
+  const uint32_t sel = 0x07060706u - __umul24(hi | (lo << 16), 0x0202u);
+  return __builtin_amdgcn_perm(hi_w, lo_w, sel);
 }
 
-// One group of four 8-bit values in a 32-bit word.  INT selects |x| keys
-// (int8) instead of sign-cleared bit patterns (fp8 / bf8).
+// Tagged keys of the four 8-bit values of one word (byte p = position p).
+// INT selects |x| keys (int8: |-128| = 128) instead of sign-cleared bit
+// patterns (fp8 / bf8).  The byte-wise |x| needs no carries across bytes:
+// for a negative byte, (x ^ 0xFF) + 1 = -x <= 128.
 template <bool INT>
-__device__ __forceinline__ uint32_t group8(uint32_t w, uint32_t& nib) {
-  uint32_t k[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t b = (w >> (8 * p)) & 0xFFu;
-    if constexpr (INT) {
-      const int v = (int)(int8_t)b;
-      k[p] = (uint32_t)(v < 0 ? -v : v);
-    } else {
-      k[p] = b & 0x7Fu;
-    }
+__device__ __forceinline__ void tags8(uint32_t w, uint32_t t[4]) {
+  uint32_t k;
+  if constexpr (INT) {
+    const uint32_t m = w & 0x80808080u, s = m >> 7;  // sign bit, and 1, of each negative byte
+    k = (w ^ (m | (m - s))) + s;                      // m | (m - s): 0xFF in each negative byte
+  } else {
+    k = w & 0x7F7F7F7Fu;
   }
-  const uint32_t m = keep_mask(k[0], k[1], k[2], k[3]);
-  const uint32_t p0 = __builtin_ctz(m), p1 = 31u - __builtin_clz(m);
-  nib = p0 | (p1 << 2);
-  return ((w >> (8 * p0)) & 0xFFu) | (((w >> (8 * p1)) & 0xFFu) << 8);
+  t[0] = __builtin_amdgcn_perm(kTagBytes, k, 0x0C0C0004u);
+  t[1] = __builtin_amdgcn_perm(kTagBytes, k, 0x0C0C0105u);
+  t[2] = __builtin_amdgcn_perm(kTagBytes, k, 0x0C0C0206u);
+  t[3] = __builtin_amdgcn_perm(kTagBytes, k, 0x0C0C0307u);
+}
+// Two groups of four 8-bit values (words a, b) -> their four kept bytes
+// (a's p0, p1, then b's) and the two 4-bit codes.
+template <bool INT>
+__device__ __forceinline__ uint32_t group8x2(uint32_t a, uint32_t b, uint32_t& na, uint32_t& nb) {
+  uint32_t ta[4], tb[4], ha, la, hb, lb;
+  tags8<INT>(a, ta);
+  tags8<INT>(b, tb);
+  top2_tags(ta[0], ta[1], ta[2], ta[3], ha, la);
+  top2_tags(tb[0], tb[1], tb[2], tb[3], hb, lb);
+  na = code_of(ha, la);
+  nb = code_of(hb, lb);
+  // selector bytes p0a, p1a, 4 + p0b, 4 + p1b with p = 3 - tag
+  const uint32_t sel = 0x07070303u - (ha + (la << 8) + (hb << 16) + (lb << 24));
+  return __builtin_amdgcn_perm(b, a, sel);
 }
 
 constexpr int kCompressThreads = 256;
@@ -104,25 +145,23 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kernel(const 
     i32x2 out;
     if constexpr (ES == 2) {
       uint32_t n0, n1;
-      out[0] = (int)group16((uint64_t)d0 | ((uint64_t)d1 << 32), n0);
-      out[1] = (int)group16((uint64_t)d2 | ((uint64_t)d3 << 32), n1);
+      out[0] = (int)group16(d0, d1, n0);
+      out[1] = (int)group16(d2, d3, n1);
       vals[q] = out;
       meta[q] = (uint8_t)(n0 | (n1 << 4));
     } else {
       uint32_t n0, n1, n2, n3;
-      const uint32_t v0 = group8<INT>(d0, n0), v1 = group8<INT>(d1, n1);
-      const uint32_t v2 = group8<INT>(d2, n2), v3 = group8<INT>(d3, n3);
-      out[0] = (int)(v0 | (v1 << 16));
-      out[1] = (int)(v2 | (v3 << 16));
+      out[0] = (int)group8x2<INT>(d0, d1, n0, n1);
+      out[1] = (int)group8x2<INT>(d2, d3, n2, n3);
       vals[q] = out;
       reinterpret_cast<uint16_t*>(meta)[q] = (uint16_t)(n0 | (n1 << 4) | (n2 << 8) | (n3 << 12));
     }
   }
 }
 
-// K-blocked layout.  Workgroup (row tile rt, block group) covers rows
-// rt*128 .. +128 of NB consecutive blocks; thread t handles chunk t % (8*NB)
-// of rows rt*128 + t/(8*NB) + (256/(8*NB))*u.  Consecutive workgroups take
+// K-blocked layout.  Workgroup (row tile rt, block group) of T threads
+// covers rows rt*128 .. +128 of NB consecutive blocks; thread t handles
+// chunk t % (8*NB) of rows rt*128 + t/(8*NB) + (T/(8*NB))*u.  Consecutive workgroups take
 // consecutive block groups of the same row tile, so the workgroups in
 // flight read one contiguous band of A (DRAM-page friendly); each writes
 // one 8 KiB run of values per block.  Chunks past K (the tail of a partial
@@ -139,24 +178,23 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kernel(const 
 // (1 or 2 KiB, contiguous) is written with 16-byte stores.
 constexpr int kKbRowsPerTile = 128;
 
-// Blocks per workgroup (NB): 16-bit types take 4 (each row's 512 contiguous
-// bytes are read by 32 lanes) when that still gives at least 1024
-// workgroups, else 1 (a 4096 x 4096 A then compresses in 14.5 us instead of
-// 16.6 us); 8-bit types always 1 (their metadata is twice as large and the
-// staging writes collide in LDS with more blocks).
+// Launch shape, measured on cold data over 2048..16384-row, 4096..16384-
+// column A: 16-bit types take NB = 2 blocks per workgroup (each row's 256
+// contiguous bytes read by 16 lanes) with 256 threads when that still gives
+// at least 1024 workgroups, else NB = 1; 8-bit types take NB = 1 with 512
+// threads.  8192 x 8192: fp16 36.4 us, int8 22.3 us.
 constexpr int64_t kKbMinWorkgroups = 1024;
+constexpr int kKbBlocks16 = 2, kKbThreads16 = 256, kKbThreads8 = 512;
 
-template <int ES, bool INT, int NB>
-__global__ __launch_bounds__(kCompressThreads) void prune_compress_kblock_kernel(const char* __restrict__ A,
-                                                                                   char* __restrict__ vals,
-                                                                                   char* __restrict__ meta,
-                                                                                   int64_t M, int64_t K,
-                                                                                   uint32_t nblk) {
+template <int ES, bool INT, int NB, int T>
+__global__ __launch_bounds__(T) void prune_compress_kblock_kernel(const char* __restrict__ A, char* __restrict__ vals,
+                                                                  char* __restrict__ meta, int64_t M, int64_t K,
+                                                                  uint32_t nblk) {
   constexpr int MB = ES == 2 ? 8 : 16;         // metadata bytes per row per block
   constexpr int CE = 16 / ES;                   // dense elements per chunk
   constexpr int GB = 128 * MB;                  // metadata bytes of one 128-row group per block
   constexpr int CPR = 8 * NB;                   // chunks per row in the tile
-  constexpr int RPR = kCompressThreads / CPR;   // rows per load round
+  constexpr int RPR = T / CPR;                  // rows per load round
   constexpr int NR = 128 / RPR;                 // load rounds
   __shared__ __attribute__((aligned(16))) char lmeta[NB * GB];
   const uint32_t nwb = (nblk + NB - 1) / NB;
@@ -169,30 +207,36 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kblock_kernel
   const int64_t kcol = b * (8 * CE) + (int64_t)c * CE;
   const bool inside = kcol < K;
   const int64_t rowbytes = K * ES;
+  // Row rr of the tile (rr = r_first + RPR*u) is row row0 + rr of A; the
+  // addresses advance by a uniform stride per round, and the bounds checks
+  // are 32-bit compares against the rows this tile has inside M.
+  const int64_t row0 = (int64_t)rt * kKbRowsPerTile;
+  const int rows_here = (int)min<int64_t>(M - row0, (int64_t)kKbRowsPerTile);
+  const int r_first = threadIdx.x / CPR;
+  const char* src = A + (row0 + r_first) * rowbytes + kcol * ES;
+  char* dst = vals + (b * M + row0 + r_first) * 64 + c * 8;
   i32x4 in[NR];
 #pragma unroll
   for (int u = 0; u < NR; ++u) {
-    const int64_t row = (int64_t)rt * kKbRowsPerTile + threadIdx.x / CPR + RPR * u;
     in[u] = i32x4{0, 0, 0, 0};
-    if (row < M && inside)
-      in[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(A + row * rowbytes + kcol * ES));
+    if (r_first + RPR * u < rows_here && inside)
+      in[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(src + (int64_t)(RPR * u) * rowbytes));
   }
   char* lm = lmeta + bi * GB;
 #pragma unroll
   for (int u = 0; u < NR; ++u) {
-    const int rr = threadIdx.x / CPR + RPR * u;  // row inside the 128-row group
-    const int64_t row = (int64_t)rt * kKbRowsPerTile + rr;
+    const int rr = r_first + RPR * u;  // row inside the 128-row group
     const int t = rr >> 4, r = rr & 15;
     const uint32_t d0 = (uint32_t)in[u][0], d1 = (uint32_t)in[u][1];
     const uint32_t d2 = (uint32_t)in[u][2], d3 = (uint32_t)in[u][3];
     i32x2 out = {0, 0};
-    const bool live = row < M && inside;  // padding rows and chunks past K: zero codes
+    const bool live = rr < rows_here && inside;  // padding rows and chunks past K: zero codes
     if constexpr (ES == 2) {
       uint8_t code = 0;
       if (live) {
         uint32_t n0, n1;
-        out[0] = (int)group16((uint64_t)d0 | ((uint64_t)d1 << 32), n0);
-        out[1] = (int)group16((uint64_t)d2 | ((uint64_t)d3 << 32), n1);
+        out[0] = (int)group16(d0, d1, n0);
+        out[1] = (int)group16(d2, d3, n1);
         code = (uint8_t)(n0 | (n1 << 4));
       }
       lm[(((r * 4 + c / 2) * 4 + t / 2) * 2 + (t & 1)) * 2 + (c & 1)] = (char)code;
@@ -200,20 +244,18 @@ __global__ __launch_bounds__(kCompressThreads) void prune_compress_kblock_kernel
       uint16_t code = 0;
       if (live) {
         uint32_t n0, n1, n2, n3;
-        const uint32_t v0 = group8<INT>(d0, n0), v1 = group8<INT>(d1, n1);
-        const uint32_t v2 = group8<INT>(d2, n2), v3 = group8<INT>(d3, n3);
-        out[0] = (int)(v0 | (v1 << 16));
-        out[1] = (int)(v2 | (v3 << 16));
+        out[0] = (int)group8x2<INT>(d0, d1, n0, n1);
+        out[1] = (int)group8x2<INT>(d2, d3, n2, n3);
         code = (uint16_t)(n0 | (n1 << 4) | (n2 << 8) | (n3 << 12));
       }
       *reinterpret_cast<uint16_t*>(lm + ((r * 4 + c / 2) * 8 + t) * 4 + (c & 1) * 2) = code;
     }
-    if (row < M && b < (int64_t)nblk) *reinterpret_cast<i32x2*>(vals + (b * M + row) * 64 + c * 8) = out;
+    if (rr < rows_here && b < (int64_t)nblk) *reinterpret_cast<i32x2*>(dst + RPR * 64 * u) = out;
   }
   __syncthreads();
   // each block's group metadata, 16 bytes per thread
 #pragma unroll
-  for (int q = threadIdx.x; q < NB * GB / 16; q += kCompressThreads) {
+  for (int q = threadIdx.x; q < NB * GB / 16; q += T) {
     const int bq = q / (GB / 16), w = q % (GB / 16);
     if (b0 + bq < (int64_t)nblk)
       reinterpret_cast<i32x4*>(meta + ((b0 + bq) * Mp + (int64_t)rt * 128) * MB)[w] =
@@ -229,10 +271,12 @@ hipError_t launch_prune_compress(const void* A, void* vals, uint32_t* meta, int6
   if (M == 0 || K == 0) return hipSuccess;
   const dim3 block(kCompressThreads);
   if (layout == SP24_LAYOUT_KBLOCK) {
+    const dim3 block(es == 2 ? kKbThreads16 : kKbThreads8);
     const int64_t kb = es == 2 ? 64 : 128;
     const int64_t nblk = (K + kb - 1) / kb;
     const int64_t row_tiles = (M + kKbRowsPerTile - 1) / kKbRowsPerTile;
-    const int nb_per_wg = (es == 2 && row_tiles * ((nblk + 3) / 4) >= kKbMinWorkgroups) ? 4 : 1;
+    const int nb_per_wg =
+        (es == 2 && row_tiles * ((nblk + kKbBlocks16 - 1) / kKbBlocks16) >= kKbMinWorkgroups) ? kKbBlocks16 : 1;
     const int64_t nwb = (nblk + nb_per_wg - 1) / nb_per_wg;
     if (row_tiles * nwb > 0x7FFFFFFFll) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(row_tiles * nwb));
@@ -240,14 +284,18 @@ hipError_t launch_prune_compress(const void* A, void* vals, uint32_t* meta, int6
     char* v = static_cast<char*>(vals);
     char* m = reinterpret_cast<char*>(meta);
     const uint32_t nb = (uint32_t)nblk;
-    if (es == 2 && nb_per_wg == 4)
-      hipLaunchKernelGGL((prune_compress_kblock_kernel<2, false, 4>), grid, block, 0, stream, a, v, m, M, K, nb);
+    if (es == 2 && nb_per_wg == kKbBlocks16)
+      hipLaunchKernelGGL((prune_compress_kblock_kernel<2, false, kKbBlocks16, kKbThreads16>), grid, block, 0, stream,
+                         a, v, m, M, K, nb);
     else if (es == 2)
-      hipLaunchKernelGGL((prune_compress_kblock_kernel<2, false, 1>), grid, block, 0, stream, a, v, m, M, K, nb);
+      hipLaunchKernelGGL((prune_compress_kblock_kernel<2, false, 1, kKbThreads16>), grid, block, 0, stream, a, v, m,
+                         M, K, nb);
     else if (is_int)
-      hipLaunchKernelGGL((prune_compress_kblock_kernel<1, true, 1>), grid, block, 0, stream, a, v, m, M, K, nb);
+      hipLaunchKernelGGL((prune_compress_kblock_kernel<1, true, 1, kKbThreads8>), grid, block, 0, stream, a, v, m, M,
+                         K, nb);
     else
-      hipLaunchKernelGGL((prune_compress_kblock_kernel<1, false, 1>), grid, block, 0, stream, a, v, m, M, K, nb);
+      hipLaunchKernelGGL((prune_compress_kblock_kernel<1, false, 1, kKbThreads8>), grid, block, 0, stream, a, v, m,
+                         M, K, nb);
     return hipGetLastError();
   }
   const int64_t nchunks = M * K * es / 16;
