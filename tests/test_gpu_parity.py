@@ -150,6 +150,19 @@ def test_compress_random(pkg, dtype, shape, layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16, wl.I8, wl.E4M3])
+@pytest.mark.parametrize("shape", [(4136, 4128), (4104, 4224)])
+def test_compress_many_workgroups(pkg, dtype, shape, layout):
+    """Shapes large enough for the K-blocked launch to give 16-bit workgroups
+    two blocks each, with a ragged last row tile, a partial last block and an
+    odd block count (the second block of the last group lies past K)."""
+    M, K = shape
+    _say(f"compress dtype={dtype} M={M} K={K} layout={layout}")
+    c = wl.random_case(17, M, 16, K, dtype, dtype)
+    check_compress(pkg, c.A, dtype, layout)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("dtype", [wl.F16, wl.BF16, wl.E4M3, wl.E5M2, wl.I8])
 def test_compress_adversarial_alphabet(pkg, dtype, layout):
     """Ties, signed zeros, extremes, subnormals and NaN in every position."""
