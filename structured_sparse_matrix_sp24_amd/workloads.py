@@ -173,6 +173,33 @@ def make(name: str, seed: int = 0, M=None, N=None, K=None) -> Workload:
     return Workload(name, M, N, K, a, b, sp["alpha"], sp["beta"], A, B, C, notes)
 
 
+def small_int_bits(shape, dtype: int, seed: int, lo: int = -1, hi: int = 1) -> np.ndarray:
+    """Integers in [lo, hi] for tensors too large to draw element by element
+    (billions of elements: fp64 normals would need tens of GB of host
+    memory).  One seeded block of a prime length P = 1,000,003 is drawn and
+    repeated over the row-major flat index, so element (i, j) is
+    block[(i * cols + j) mod P]; P shares no factor with any tile size.
+    Stored as `dtype`; exact in every format for the ranges the tests use.
+    With |a|, |b| <= 1 every partial sum of a product is an integer below
+    2^24 for K <= 2^25, so such products are exact in fp32."""
+    shape = tuple(int(x) for x in shape)
+    v = _rng(seed, 4).integers(lo, hi + 1, 1_000_003)
+    if dtype == I8:
+        bits = v.astype(np.int8)
+    elif dtype == F16:
+        bits = v.astype(np.float16).view(np.uint16)
+    elif dtype == BF16:
+        bits = (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    else:
+        bits = quantize(v.astype(np.float64), dtype)
+    out = np.empty(shape, dtype=bits.dtype)
+    flat = out.reshape(-1)
+    for s in range(0, flat.size, bits.size):  # repeat the block over the flat index
+        n = min(bits.size, flat.size - s)
+        flat[s:s + n] = bits[:n]
+    return out
+
+
 def random_case(seed: int, M: int, N: int, K: int, a_type: int, b_type: int, beta: float = 0.0,
                 alpha: float = 1.0, std: float = 1.0) -> Workload:
     """Seeded random dense-A case of an arbitrary shape (for parity sweeps)."""

@@ -415,6 +415,62 @@ def test_gemm_K_zero_out16_bias(pkg, out):
     assert (np.abs(got - ref) <= 1e-6 * np.abs(ref) + grid_spacing(ref, out)).all()
 
 
+# ---- the largest shapes the boundary accepts ---------------------------------
+# The C ABI bounds every buffer range one workgroup addresses below 2 GiB:
+# N * sizeof(b) * 128 (a k-step of B stored K x N, 8-bit), 256 * K/2 * sizeof(a)
+# (a row tile of A in the ROW layout) and 256 * K * sizeof(b) (a column tile
+# of B stored N x K).  These run each limit at its largest accepted value,
+# with integer inputs so the exact product is known, and check sampled
+# outputs (whole first and last rows and columns included).
+MAX_BYTES = 0x7FFFFF00  # the largest per-workgroup range the library accepts
+
+
+def _max_case(pkg, M, N, K, dtype, layout, b_layout, lim):
+    hi = 127 if dtype == wl.I8 else 1
+    A = wl.small_int_bits((M, K), dtype, 31, -hi, hi)
+    B = wl.small_int_bits((K, N), dtype, 32, -hi, hi)
+    assert lim <= MAX_BYTES
+    ov, om = check_compress(pkg, A, dtype, layout)
+    D = run_gemm(pkg, ov, om, dtype, B, dtype, layout=layout, b_layout=b_layout)
+    if K <= 4096:  # N is the large dimension: sampled points
+        w = wl.Workload(f"max_{M}x{N}x{K}", M, N, K, dtype, dtype, 1.0, 0.0, A, B, None)
+        check_gemm_sampled(D, ov, om, w, n=64)
+        return
+    # K is the large dimension: whole output rows (first, last and two
+    # others), each from the oracle's full product of that one row of A,
+    # which streams B once per row instead of once per point
+    rows = sorted({0, M - 1, M // 3, (2 * M) // 3})
+    got = D[rows].cpu().numpy().astype(np.float64)
+    for n, i in enumerate(rows):
+        ref, S = oracle.gemm_f64(ov[i:i + 1], om[i:i + 1], dtype, B, dtype)
+        err = np.abs(got[n] - ref[0])
+        assert (err <= 1e-4 * S[0] + 1e-6).all(), f"row {i}: worst ratio {np.max(err / (S[0] + 1e-30)):.3g}"
+
+
+@pytest.mark.parametrize("dtype", [wl.F16, wl.I8])
+def test_gemm_largest_n(pkg, dtype):
+    """N at the limit for B stored K x N: 128 rows of B just below 2 GiB."""
+    es = wl.ESIZE[dtype]
+    N = (MAX_BYTES // 128 // es) // 16 * 16
+    M, K = (20, 96) if es == 2 else (16, 160)  # a partial last k-step either way
+    _say(f"gemm largest N dtype={dtype} M={M} N={N} K={K}")
+    _max_case(pkg, M, N, K, dtype, KBLOCK, KN, N * es * 128)
+
+
+def test_gemm_largest_k_row_layout(pkg):
+    """K at the limit for the ROW layout: a 256-row tile of A just below 2 GiB."""
+    K = (MAX_BYTES // 256 // 2 * 2) // 32 * 32
+    _say(f"gemm largest K (ROW) M=40 N=72 K={K}")
+    _max_case(pkg, 40, 72, K, wl.F16, ROW, KN, 256 * K // 2 * 2)
+
+
+def test_gemm_largest_k_b_transposed(pkg):
+    """K at the limit for B stored N x K: a 256-column tile of B just below 2 GiB."""
+    K = (MAX_BYTES // 256 // 2) // 32 * 32
+    _say(f"gemm largest K (B N x K) M=24 N=72 K={K}")
+    _max_case(pkg, 24, 72, K, wl.F16, KBLOCK, NK, 256 * K * 2)
+
+
 def test_gemm_gpu_compressed_input(pkg):
     """Compress on the GPU and multiply the result directly."""
     _say("gemm on GPU-compressed input")
