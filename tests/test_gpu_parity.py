@@ -471,6 +471,42 @@ def test_gemm_largest_k_b_transposed(pkg):
     _max_case(pkg, 24, 72, K, wl.F16, KBLOCK, NK, 256 * K * 2)
 
 
+def test_operands_past_4gib(pkg):
+    """Compressed A larger than 4 GiB (fp16 131112 x 40992: 10.7 GB dense,
+    5.4 GB of values), so byte offsets of later K-blocks need more than 32
+    bits.  Compress is checked bit-exact on the first, a middle and the last
+    (ragged, 40-row) 128-row group of every block; the product on whole
+    output rows of those groups."""
+    M, K, N = 131072 + 40, 40960 + 32, 72
+    dtype = wl.F16
+    _say(f"operands past 4 GiB: M={M} K={K} N={N}")
+    A = wl.small_int_bits((M, K), dtype, 41)
+    B = wl.small_int_bits((K, N), dtype, 42)
+    At = to_dev(A, dtype)
+    vals, meta = pkg.prune_compress(At, dtype, KBLOCK)
+    del At
+    torch.cuda.synchronize()
+    nblk, VE, Mp = -(-K // 64), 32, -(-M // 128) * 128
+    assert tuple(vals.shape) == (nblk, M, VE) and tuple(meta.shape) == (nblk, Mp, 2)
+    groups = [(0, 128), (65536, 128), (131072, 40)]
+    for r0, g in groups:
+        ov, om = oracle.prune_compress(A[r0:r0 + g], dtype)
+        ev, em = row_to_kblock(ov, om, dtype)
+        gv = to_host_bits(vals[:, r0:r0 + g, :], dtype)
+        gm = meta[:, r0:r0 + 128, :].cpu().numpy().view(np.uint32)
+        assert np.array_equal(gm, em), f"metadata of rows {r0}.. differs"
+        assert np.array_equal(gv.view(ev.dtype), ev), f"values of rows {r0}.. differs"
+    D = pkg.gemm(vals, meta, to_dev(B, dtype), None, a_type=dtype, b_type=dtype, layout=KBLOCK)
+    torch.cuda.synchronize()
+    for r0, g in groups:
+        rows = [r0, r0 + g - 1]
+        ov, om = oracle.prune_compress(A[rows], dtype)
+        ref, S = oracle.gemm_f64(ov, om, dtype, B, dtype)
+        got = D[rows].cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref)
+        assert (err <= 1e-4 * S + 1e-6).all(), f"rows {rows}: worst ratio {np.max(err / (S + 1e-30)):.3g}"
+
+
 def test_gemm_gpu_compressed_input(pkg):
     """Compress on the GPU and multiply the result directly."""
     _say("gemm on GPU-compressed input")
