@@ -118,6 +118,56 @@ def cpu_baseline(w, rows, max_threads=16):
     }
 
 
+def measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream, launches=20):
+    """The calls adjacent to the hot path, each timed over back-to-back
+    launches between two HIP events on the launch stream: sp24_decompress
+    (bytes: values + metadata + dense A), sp24_validate_meta (bytes: metadata)
+    and, for floating inputs, sp24_gemm_ex with a 16-bit output and a bias."""
+    import torch
+    from structured_sparse_matrix_sp24_amd import workloads as wl
+    sh = stream.cuda_stream
+    es = wl.ESIZE[w.a_type]
+    cbytes = pkg.sp24_values_bytes(w.M, w.K, w.a_type, layout) + pkg.sp24_meta_bytes(w.M, w.K, w.a_type, layout)
+    mbytes = pkg.sp24_meta_bytes(w.M, w.K, w.a_type, layout)
+    dense = torch.empty(w.M * w.K * es, dtype=torch.uint8, device="cuda:0")
+    bad = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3  # us
+
+    def check(st, what):
+        if st:
+            raise pkg.Sp24Error(st, what)
+
+    out = {}
+    us = timed(lambda: check(pkg.sp24_decompress(vals.data_ptr(), meta.data_ptr(), dense.data_ptr(), w.M, w.K,
+                                                  w.a_type, layout, sh), "sp24_decompress"), launches)
+    nb = cbytes + w.M * w.K * es
+    out["decompress"] = {"us": round(us, 2), "bytes": nb, "GB/s": round(nb / us / 1e3, 1),
+                         "frac_hbm": round(nb / us / 1e3 / PEAK_HBM_GBPS, 4)}
+    us = timed(lambda: check(pkg.sp24_validate_meta(meta.data_ptr(), w.M, w.K, w.a_type, layout, bad.data_ptr(),
+                                                     sh), "sp24_validate_meta"), launches)
+    out["validate_meta"] = {"us": round(us, 2), "bytes": mbytes, "GB/s": round(mbytes / us / 1e3, 1),
+                            "frac_hbm": round(mbytes / us / 1e3 / PEAK_HBM_GBPS, 4)}
+    if w.a_type != wl.I8:
+        D16 = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda:0")
+        bias = torch.ones(w.N, dtype=torch.float32, device="cuda:0")
+        us = timed(lambda: check(pkg.sp24_gemm_ex(vals.data_ptr(), meta.data_ptr(), w.a_type, layout, B.data_ptr(),
+                                                  w.b_type, b_layout, D16.data_ptr(), wl.F16, bias.data_ptr(), w.M,
+                                                  w.N, w.K, 1.0, 0.0, None, 0, sh), "sp24_gemm_ex"), 5)
+        tf = 2.0 * w.M * w.N * w.K / (us * 1e-6) / 1e12
+        out["gemm_ex_f16_out_bias"] = {"us": round(us, 1), "TFLOP/s": round(tf, 1)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +182,9 @@ def main():
                     help="how B is stored: K x N (kn) or transposed, N x K (nk, e.g. activations)")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the oracle sample (default: sized to ~15 s)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--next-rows", action="store_true",
+                    help="also time the adjacent calls (decompress, validate_meta, 16-bit output with bias) "
+                         "after the timed steps and add them to the line as next_rows")
     ap.add_argument("--gemm-only-launches", type=int, default=0,
                     help="after the timed steps, launch only the GEMM this many times (for profilers)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -238,6 +291,7 @@ def main():
     for _ in range(args.gemm_only_launches):
         gemm()
     torch.cuda.synchronize()
+    next_rows = measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream) if args.next_rows else None
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     flop = 2.0 * w.M * w.N * w.K
@@ -293,6 +347,8 @@ def main():
         "roofline": roof,
         "kernel_src_hash": khash,
     }
+    if next_rows is not None:
+        res["next_rows"] = next_rows
     if not args.no_cpu:
         rows = args.cpu_rows
         if rows is None:

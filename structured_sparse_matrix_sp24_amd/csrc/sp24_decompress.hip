@@ -121,36 +121,53 @@ __device__ __forceinline__ void add_wave_count(int n, unsigned long long* out) {
 
 __global__ void zero_u64_kernel(unsigned long long* p) { *p = 0ull; }
 
-// Row-major layout: one 32-bit word (8 groups) per thread, grid-stride.
+// Row-major layout: four 32-bit words (32 groups) per thread and load,
+// grid-stride; the last nwords % 4 words one by one.
 __global__ __launch_bounds__(256) void validate_row_kernel(const uint32_t* __restrict__ meta, int64_t nwords,
                                                             unsigned long long* out) {
   int bad = 0;
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nwords; q += (int64_t)gridDim.x * blockDim.x)
-    bad += bad_groups_in(meta[q], 8);
+  const int64_t nq = nwords / 4, stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int64_t q = t0; q < nq; q += stride) {
+    const i32x4 v = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(meta) + q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bad += bad_groups_in((uint32_t)v[e], 8);
+  }
+  for (int64_t q = 4 * nq + t0; q < nwords; q += stride) bad += bad_groups_in(meta[q], 8);
   add_wave_count(bad, out);
 }
 
-// K-blocked layout: one code word (row i < M, word g) of one block per thread,
-// grid-stride; only groups inside K are counted (the tail of a partial last
-// block and the padding rows hold zero codes).
+// K-blocked layout: one 16-byte piece of one block's metadata per thread and
+// load (block b over grid y, pieces over grid x, both grid-stride).  In a
+// 128-row group, code word x (16-bit units for 16-bit types, 32-bit for 8-bit
+// ones) belongs to row 16t + r and word g of the row's block, with t = x & 7,
+// g = (x >> 3) & 3, r = (x >> 5) & 15, so a piece holds 8 (or 4) consecutive
+// t of one (g, r).  Only groups inside K of rows below M are counted (the
+// tail of a partial last block and the padding rows hold zero codes).
 template <int ES>
 __global__ __launch_bounds__(256) void validate_kblock_kernel(const char* __restrict__ meta, int64_t M, int64_t K,
                                                                int64_t nblk, unsigned long long* out) {
   constexpr int MB = ES == 2 ? 8 : 16, KB = ES == 2 ? 64 : 128, GPW = KB / 16;  // groups per word
+  constexpr int WPP = ES == 2 ? 8 : 4;                                             // words per 16-byte piece
+  constexpr int PPG = 128 * MB / 16;                                               // pieces per 128-row group
   const int64_t Mp = (M + 127) / 128 * 128;
-  const int64_t total = nblk * M * 4;
+  const int64_t ppb = Mp * MB / 16;                                                // pieces per block
   int bad = 0;
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (int64_t)gridDim.x * blockDim.x) {
-    const int g = (int)(q & 3);
-    const int64_t i = (q >> 2) % M, b = (q >> 2) / M;
-    const int rr = (int)(i & 127), t = rr >> 4, r = rr & 15;
-    const char* mgroup = meta + (b * Mp + (i & ~127ll)) * MB;
-    uint32_t w;
-    if constexpr (ES == 2) w = *reinterpret_cast<const uint16_t*>(mgroup + (((r * 4 + g) * 4 + t / 2) * 2 + (t & 1)) * 2);
-    else w = *reinterpret_cast<const uint32_t*>(mgroup + ((r * 4 + g) * 8 + t) * 4);
-    const int64_t col0 = b * KB + (int64_t)g * (KB / 4);  // first dense column of the word
-    const int64_t inside = (K - col0) / 4;                // groups of the word inside K
-    bad += bad_groups_in(w, inside >= GPW ? GPW : (inside > 0 ? (int)inside : 0));
+  for (int64_t b = blockIdx.y; b < nblk; b += gridDim.y) {
+    const i32x4* blk = reinterpret_cast<const i32x4*>(meta + b * Mp * MB);
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < ppb; c += (int64_t)gridDim.x * blockDim.x) {
+      const i32x4 v = __builtin_nontemporal_load(blk + c);
+      const int x0 = (int)(c % PPG) * WPP;             // first word of the piece in its group
+      const int64_t row0 = (c / PPG) * 128 + (x0 >> 5 & 15);  // row of t = 0
+      const int g = (x0 >> 3) & 3, t0 = x0 & 7;
+      const int64_t inside = (K - (b * KB + (int64_t)g * (KB / 4))) / 4;  // groups of word g inside K
+      const int ng = inside >= GPW ? GPW : (inside > 0 ? (int)inside : 0);
+#pragma unroll
+      for (int e = 0; e < WPP; ++e) {
+        const uint32_t w = ES == 2 ? ((uint32_t)v[e / 2] >> (16 * (e & 1))) & 0xFFFFu : (uint32_t)v[e];
+        if (row0 + 16 * (t0 + e) < M) bad += bad_groups_in(w, ng);
+      }
+    }
   }
   add_wave_count(bad, out);
 }
@@ -194,15 +211,15 @@ hipError_t launch_validate(const uint32_t* meta, int64_t M, int64_t K, int dtype
   if (layout == SP24_LAYOUT_KBLOCK) {
     const int64_t kb = es == 2 ? 64 : 128;
     const int64_t nblk = (K + kb - 1) / kb;
-    const int64_t total = nblk * M * 4;
-    const unsigned grid = (unsigned)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+    const int64_t ppb = (M + 127) / 128 * 128 * (es == 2 ? 8 : 16) / 16;  // 16-byte pieces per block
+    const dim3 grid((unsigned)((ppb + 255) / 256 < 64 ? (ppb + 255) / 256 : 64), (unsigned)(nblk < 1024 ? nblk : 1024));
     const char* m = reinterpret_cast<const char*>(meta);
-    if (es == 2) hipLaunchKernelGGL((validate_kblock_kernel<2>), dim3(grid), dim3(256), 0, stream, m, M, K, nblk, out);
-    else hipLaunchKernelGGL((validate_kblock_kernel<1>), dim3(grid), dim3(256), 0, stream, m, M, K, nblk, out);
+    if (es == 2) hipLaunchKernelGGL((validate_kblock_kernel<2>), grid, dim3(256), 0, stream, m, M, K, nblk, out);
+    else hipLaunchKernelGGL((validate_kblock_kernel<1>), grid, dim3(256), 0, stream, m, M, K, nblk, out);
     return hipGetLastError();
   }
   const int64_t nwords = M * (K / 32);
-  const unsigned grid = (unsigned)((nwords + 255) / 256 < 4096 ? (nwords + 255) / 256 : 4096);
+  const unsigned grid = (unsigned)((nwords / 4 + 255) / 256 < 2048 ? (nwords / 4 + 255) / 256 + 1 : 2048);
   hipLaunchKernelGGL(validate_row_kernel, dim3(grid), dim3(256), 0, stream, meta, nwords, out);
   return hipGetLastError();
 }

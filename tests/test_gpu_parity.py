@@ -582,7 +582,7 @@ def test_decompress_matches_oracle(pkg, dtype, shape, layout):
 
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("dtype", [wl.F16, wl.I8])
-@pytest.mark.parametrize("shape", [(1, 32), (129, 160), (300, 4096), (70, 96)])
+@pytest.mark.parametrize("shape", [(1, 32), (129, 160), (300, 4096), (70, 96), (1000, 4160), (3, 8224)])
 def test_validate_meta_counts_like_oracle(pkg, dtype, shape, layout):
     M, K = shape
     _say(f"validate dtype={dtype} M={M} K={K} layout={layout}")
