@@ -102,15 +102,14 @@ __global__ __launch_bounds__(kDecThreads) void decompress_kblock_kernel(const ch
 }
 
 // ---- validation ---------------------------------------------------------------
-// Groups, among the first `ngroups` 4-bit codes of w, whose codes are not
-// strictly increasing (p0 >= p1).
-__device__ __forceinline__ int bad_groups_in(uint32_t w, int ngroups) {
-  int bad = 0;
-  for (int g = 0; g < ngroups; ++g) {
-    const uint32_t nib = (w >> (4 * g)) & 0xFu;
-    bad += (nib & 3u) >= ((nib >> 2) & 3u);
-  }
-  return bad;
+// Groups of a 32-bit code word (eight 4-bit codes p0 | p1 << 2) whose codes
+// are not strictly increasing (p0 >= p1), among those whose nibbles `mask`
+// covers; all eight at once.  Per nibble, (p0 | 4) - p1 lies in
+// 1..7, so nothing borrows across nibbles, and its bit 2 is set exactly when
+// p0 >= p1.
+__device__ __forceinline__ int bad_groups_masked(uint32_t w, uint32_t mask) {
+  const uint32_t d = ((w & 0x33333333u) | 0x44444444u) - ((w >> 2) & 0x33333333u);
+  return __builtin_popcount(d & 0x44444444u & mask);
 }
 
 // Sum over the wave, then one 64-bit vector atomic per wave.
@@ -131,9 +130,9 @@ __global__ __launch_bounds__(256) void validate_row_kernel(const uint32_t* __res
   for (int64_t q = t0; q < nq; q += stride) {
     const i32x4 v = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(meta) + q);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) bad += bad_groups_in((uint32_t)v[e], 8);
+    for (int e = 0; e < 4; ++e) bad += bad_groups_masked((uint32_t)v[e], 0xFFFFFFFFu);
   }
-  for (int64_t q = 4 * nq + t0; q < nwords; q += stride) bad += bad_groups_in(meta[q], 8);
+  for (int64_t q = 4 * nq + t0; q < nwords; q += stride) bad += bad_groups_masked(meta[q], 0xFFFFFFFFu);
   add_wave_count(bad, out);
 }
 
@@ -162,10 +161,15 @@ __global__ __launch_bounds__(256) void validate_kblock_kernel(const char* __rest
       const int g = (x0 >> 3) & 3, t0 = x0 & 7;
       const int64_t inside = (K - (b * KB + (int64_t)g * (KB / 4))) / 4;  // groups of word g inside K
       const int ng = inside >= GPW ? GPW : (inside > 0 ? (int)inside : 0);
+      const uint32_t wmask = ng == 8 ? 0xFFFFFFFFu : (1u << (4 * ng)) - 1u;  // nibbles of one word inside K
 #pragma unroll
-      for (int e = 0; e < WPP; ++e) {
-        const uint32_t w = ES == 2 ? ((uint32_t)v[e / 2] >> (16 * (e & 1))) & 0xFFFFu : (uint32_t)v[e];
-        if (row0 + 16 * (t0 + e) < M) bad += bad_groups_in(w, ng);
+      for (int e = 0; e < 4; ++e) {  // one 32-bit element: two 16-bit words (rows t, t+1) or one 32-bit word
+        uint32_t mask;
+        if constexpr (ES == 2)
+          mask = (row0 + 16 * (t0 + 2 * e) < M ? wmask : 0u) | (row0 + 16 * (t0 + 2 * e + 1) < M ? wmask << 16 : 0u);
+        else
+          mask = row0 + 16 * (t0 + e) < M ? wmask : 0u;
+        bad += bad_groups_masked((uint32_t)v[e], mask);
       }
     }
   }
