@@ -17,6 +17,7 @@ namespace sp24 {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecUnroll = 4;
+constexpr int kDecKbThreads = 512;  // K-blocked kernel
 
 // One group of four 16-bit values from its two kept values and 4-bit code
 // (p0 in bits 0-1, p1 in bits 2-3); the second value wins a shared slot.
@@ -69,35 +70,47 @@ __global__ __launch_bounds__(kDecThreads) void decompress_row_kernel(const i32x2
   }
 }
 
-// K-blocked layout: workgroup (row tile rt, block b) covers rows rt*128 ..
-// +128 of block b, thread t chunk t%8 of rows rt*128 + t/8 + 32u; the codes
-// are read from their interleaved position in the row's 128-row group.
-template <int ES>
-__global__ __launch_bounds__(kDecThreads) void decompress_kblock_kernel(const char* __restrict__ vals,
-                                                                          const char* __restrict__ meta,
-                                                                          char* __restrict__ A, int64_t M, int64_t K,
-                                                                          uint32_t nblk) {
+// K-blocked layout: workgroup (row tile rt, block group) of T threads covers
+// rows rt*128 .. +128 of NB consecutive blocks; thread t handles chunk
+// t % (8*NB) of rows rt*128 + t/(8*NB) + (T/(8*NB))*u, with one base address
+// per thread advanced by a uniform stride per round; the codes are read from
+// their interleaved position in the row's 128-row group.  (An earlier form
+// that recomputed each round's 64-bit addresses from the row index gave
+// different outputs from run to run on 8192 x 8192 inputs while passing on
+// small ones; this form gave the same, oracle-exact output in every run.)
+template <int ES, int NB, int T>
+__global__ __launch_bounds__(T) void decompress_kblock_kernel(const char* __restrict__ vals,
+                                                               const char* __restrict__ meta,
+                                                               char* __restrict__ A, int64_t M, int64_t K,
+                                                               uint32_t nblk) {
   constexpr int MB = ES == 2 ? 8 : 16, CE = 16 / ES;
-  const int64_t b = blockIdx.x % nblk;
-  const uint32_t rt = blockIdx.x / nblk;
+  constexpr int CPR = 8 * NB, RPR = T / CPR, NR = 128 / RPR;
+  const uint32_t nwb = (nblk + NB - 1) / NB;
+  const int64_t b = (int64_t)(blockIdx.x % nwb) * NB + (threadIdx.x % CPR) / 8;
+  const uint32_t rt = blockIdx.x / nwb;
   const int64_t Mp = (M + 127) / 128 * 128;
   const int c = threadIdx.x & 7;
   const int64_t kcol = b * (8 * CE) + (int64_t)c * CE;
   if (kcol >= K) return;
   const char* mgroup = meta + (b * Mp + (int64_t)rt * 128) * MB;
+  const int64_t row0 = (int64_t)rt * 128;
+  const int rows_here = (int)min<int64_t>(M - row0, 128);
+  const int r_first = threadIdx.x / CPR;
+  const char* src = vals + (b * M + row0 + r_first) * 64 + c * 8;
+  char* dst = A + (row0 + r_first) * K * ES + kcol * ES;
 #pragma unroll
-  for (int u = 0; u < kDecUnroll; ++u) {
-    const int rr = (threadIdx.x >> 3) + 32 * u;
-    const int64_t row = (int64_t)rt * 128 + rr;
-    if (row >= M) break;
+  for (int u = 0; u < NR; ++u) {
+    const int rr = r_first + RPR * u;
+    if (rr >= rows_here) break;
     const int t = rr >> 4, r = rr & 15;
-    const i32x2 v = __builtin_nontemporal_load(reinterpret_cast<const i32x2*>(vals + (b * M + row) * 64 + c * 8));
+    const i32x2 v = __builtin_nontemporal_load(reinterpret_cast<const i32x2*>(src + RPR * 64 * u));
     uint32_t code;
     if constexpr (ES == 2)
       code = *reinterpret_cast<const uint8_t*>(mgroup + (((r * 4 + c / 2) * 4 + t / 2) * 2 + (t & 1)) * 2 + (c & 1));
     else
       code = *reinterpret_cast<const uint16_t*>(mgroup + ((r * 4 + c / 2) * 8 + t) * 4 + (c & 1) * 2);
-    __builtin_nontemporal_store(expand_chunk<ES>(v, code), reinterpret_cast<i32x4*>(A + row * K * ES + kcol * ES));
+    __builtin_nontemporal_store(expand_chunk<ES>(v, code),
+                                reinterpret_cast<i32x4*>(dst + (int64_t)(RPR * u) * K * ES));
   }
 }
 
@@ -185,13 +198,22 @@ hipError_t launch_decompress(const void* vals, const uint32_t* meta, void* A, in
   if (layout == SP24_LAYOUT_KBLOCK) {
     const int64_t kb = es == 2 ? 64 : 128;
     const int64_t nblk = (K + kb - 1) / kb, row_tiles = (M + 127) / 128;
-    if (row_tiles * nblk > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(row_tiles * nblk));
+    // 16-bit types: two blocks (256 contiguous bytes of a dense row) per
+    // workgroup while that leaves at least 1024 workgroups; 512 threads
+    const int nb = es == 2 && row_tiles * ((nblk + 1) / 2) >= 1024 ? 2 : 1;
+    const int64_t nwb = (nblk + nb - 1) / nb;
+    if (row_tiles * nwb > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(row_tiles * nwb)), blk(kDecKbThreads);
     const char* v = static_cast<const char*>(vals);
     const char* m = reinterpret_cast<const char*>(meta);
     char* a = static_cast<char*>(A);
-    if (es == 2) hipLaunchKernelGGL((decompress_kblock_kernel<2>), grid, block, 0, stream, v, m, a, M, K, (uint32_t)nblk);
-    else hipLaunchKernelGGL((decompress_kblock_kernel<1>), grid, block, 0, stream, v, m, a, M, K, (uint32_t)nblk);
+    const uint32_t n = (uint32_t)nblk;
+    if (es == 2 && nb == 2)
+      hipLaunchKernelGGL((decompress_kblock_kernel<2, 2, kDecKbThreads>), grid, blk, 0, stream, v, m, a, M, K, n);
+    else if (es == 2)
+      hipLaunchKernelGGL((decompress_kblock_kernel<2, 1, kDecKbThreads>), grid, blk, 0, stream, v, m, a, M, K, n);
+    else
+      hipLaunchKernelGGL((decompress_kblock_kernel<1, 1, kDecKbThreads>), grid, blk, 0, stream, v, m, a, M, K, n);
     return hipGetLastError();
   }
   const int64_t nchunks = M * K * es / 16;

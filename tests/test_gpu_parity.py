@@ -582,6 +582,31 @@ def test_decompress_matches_oracle(pkg, dtype, shape, layout):
 
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("dtype", [wl.F16, wl.I8])
+@pytest.mark.parametrize("shape", [(8192, 8192), (4136, 4128)])
+def test_decompress_full_size_repeatable(pkg, dtype, shape, layout):
+    """Decompression of a full benchmark-size A (and a ragged one whose 16-bit
+    workgroups take two blocks), three times into fresh buffers, each compared
+    with the oracle over the whole output: a kernel that is right on small
+    shapes can still be wrong, or differ from run to run, at full size."""
+    M, K = shape
+    _say(f"decompress full size dtype={dtype} M={M} K={K} layout={layout}")
+    A = wl.small_int_bits((M, K), dtype, 51, -127, 127) if dtype == wl.I8 else \
+        wl.random_case(53, M, 16, K, dtype, dtype).A
+    ov, om = oracle.prune_compress(A, dtype)
+    expect = oracle.decompress(ov, om, dtype)
+    ev, em = in_layout(ov, om, dtype, layout)
+    V = to_dev(ev, dtype)
+    Mt = torch.from_numpy(np.ascontiguousarray(em).view(np.int32)).to(DEV)
+    for rep in range(3):
+        D = pkg.decompress(V, Mt, K, dtype, layout)
+        torch.cuda.synchronize()
+        got = to_host_bits(D, dtype)
+        assert np.array_equal(got, expect), f"run {rep}: {int((got != expect).sum())} elements differ"
+        del D
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("dtype", [wl.F16, wl.I8])
 @pytest.mark.parametrize("shape", [(1, 32), (129, 160), (300, 4096), (70, 96), (1000, 4160), (3, 8224)])
 def test_validate_meta_counts_like_oracle(pkg, dtype, shape, layout):
     M, K = shape
