@@ -538,6 +538,10 @@ def test_workload_full_size(pkg, name, b_layout):
     assert np.array_equal(meta_d.cpu().numpy().view(np.uint32), em), "metadata differs"
     assert np.array_equal(to_host_bits(vals_d, w.a_type).view(ev.dtype), ev), "values differ"
     del ev, em
+    for _ in range(2):  # the same bits on every run
+        v2, m2 = pkg.prune_compress(A, w.a_type, KBLOCK)
+        assert torch.equal(v2.view(torch.uint8), vals_d.view(torch.uint8)) and torch.equal(m2, meta_d)
+        del v2, m2
     if name == "tiny_f16":
         assert (om == 0x88888888).all()
     if name == "i8_8192":
@@ -554,6 +558,12 @@ def test_workload_full_size(pkg, name, b_layout):
         check_gemm_full(pkg, ov, om, w.a_type, w.B, w.b_type, w.C, w.alpha, w.beta, b_layout=b_layout)
     else:
         check_gemm_sampled(D, ov, om, w)
+    for _ in range(2):  # the summation order is fixed, so every run gives the same bits
+        C2 = None if w.C is None else torch.from_numpy(w.C).to(DEV)
+        D2 = pkg.gemm(vals_d, meta_d, B, C2, alpha=w.alpha, beta=w.beta, a_type=w.a_type, b_type=w.b_type)
+        torch.cuda.synchronize()
+        assert torch.equal(D2.view(torch.int32), D.view(torch.int32)), "product differs between runs"
+        del D2, C2
 
 
 # ---- decompression and metadata validation -------------------------------------------
