@@ -566,6 +566,38 @@ def test_workload_full_size(pkg, name, b_layout):
         del D2, C2
 
 
+@pytest.mark.parametrize("name", ["f16_8192", "i8_8192", "bf16_linear_n16"])
+def test_workload_full_size_row_layout(pkg, name):
+    """The benchmark workloads through the ROW (row-major) compressed layout:
+    compress bit-exact, the product on sampled outputs, both repeated."""
+    _say(f"workload {name} (ROW layout): generating inputs")
+    w = wl.make(name)
+    A = to_dev(w.A, w.a_type)
+    ov, om = oracle.prune_compress(w.A, w.a_type)
+    ref_v = None
+    for _ in range(2):
+        vals_d, meta_d = pkg.prune_compress(A, w.a_type, ROW)
+        torch.cuda.synchronize()
+        if ref_v is None:
+            assert np.array_equal(meta_d.cpu().numpy().view(np.uint32), om), "metadata differs"
+            assert np.array_equal(to_host_bits(vals_d, w.a_type).view(ov.dtype), ov), "values differ"
+            ref_v, ref_m = vals_d, meta_d
+        else:
+            assert torch.equal(vals_d.view(torch.uint8), ref_v.view(torch.uint8)) and torch.equal(meta_d, ref_m)
+    del A
+    B = b_on_dev(w.B, w.b_type, KN)
+    D0 = None
+    for _ in range(2):
+        C = None if w.C is None else torch.from_numpy(w.C).to(DEV)
+        D = pkg.gemm(ref_v, ref_m, B, C, alpha=w.alpha, beta=w.beta, a_type=w.a_type, b_type=w.b_type)
+        torch.cuda.synchronize()
+        if D0 is None:
+            check_gemm_sampled(D, ov, om, w)
+            D0 = D
+        else:
+            assert torch.equal(D.view(torch.int32), D0.view(torch.int32)), "product differs between runs"
+
+
 # ---- decompression and metadata validation -------------------------------------------
 def _rand_meta(seed, M, K):
     """Random code words: every code value, valid and invalid groups alike."""
