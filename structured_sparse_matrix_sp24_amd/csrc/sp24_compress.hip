@@ -7,22 +7,26 @@
 // the library's reading (the pages leave pruning to an offline pass): the
 // two largest magnitudes, the lower position winning a tie.
 //
-// Design: the whole problem is a flat stream.  Because K % 32 == 0, every
-// 16-byte chunk of A (8 fp16/bf16 = 2 groups, or 16 8-bit values = 4 groups)
-// maps to exactly 8 bytes of A_vals and 1 (16-bit) or 2 (8-bit) bytes of
-// metadata at the same chunk index, independent of M and K.  Each lane reads
-// whole 16-byte chunks with consecutive lanes on consecutive chunks, so every
-// wave instruction (load and store) is one contiguous span.  No MFMA, no LDS:
-// the kernel is bound by HBM bandwidth.  A is read with non-temporal loads
-// (it is not reused); the outputs are written with ordinary stores, which
-// measured about 5 % faster than non-temporal ones for the 8192^2 fp16 A.
+// Design: the whole problem is a flat stream bound by HBM bandwidth (no
+// MFMA).  Because K % 32 == 0, every 16-byte chunk of A (8 fp16/bf16 = 2
+// groups, or 16 8-bit values = 4 groups) maps to exactly 8 bytes of A_vals and
+// 1 (16-bit) or 2 (8-bit) bytes of metadata at the same chunk index,
+// independent of M and K.  In the row-major layout each lane reads whole
+// 16-byte chunks with consecutive lanes on consecutive chunks, so every wave
+// instruction (load and store) is one contiguous span.  A is read with
+// non-temporal loads (it is not reused); the outputs are written with
+// ordinary stores, which measured about 5 % faster than non-temporal ones for
+// the 8192^2 fp16 A.  The selection itself is kept short (byte permutes and
+// three-input max / median), since with pairwise rank counting the 8-bit
+// kernels were bound by the vector ALU rather than by HBM.
 //
 // The K-blocked output layout (one k-step of the GEMM = KB dense columns per
 // block, all M rows of a block stored together) uses a 2-D mapping instead:
-// a lane owns one 16-byte chunk of one row's block (8 chunks per block), so
-// eight consecutive lanes read one row's 128 contiguous bytes and a wave
-// writes eight consecutive rows of a block, i.e. one contiguous 512-byte run
-// of values and one 64- or 128-byte run of metadata.
+// a lane owns one 16-byte chunk of one row's block, so 8 * NB consecutive
+// lanes read 128 * NB contiguous bytes of a row, and the values of the
+// workgroup's 128 rows go out as one 8 KiB run per block.  The metadata of a
+// 128-row group is interleaved for the product's fragment reads, so it is
+// gathered in LDS and written as one contiguous 1 or 2 KiB run per block.
 #include "sp24_internal.hpp"
 
 namespace sp24 {
