@@ -645,6 +645,14 @@ def test_decompress_full_size_repeatable(pkg, dtype, shape, layout):
         got = to_host_bits(D, dtype)
         assert np.array_equal(got, expect), f"run {rep}: {int((got != expect).sum())} elements differ"
         del D
+    # validation at the same size: the compressor's codes are all valid, and
+    # arbitrary codes are counted as the oracle counts them
+    assert int(pkg.validate_meta(Mt, M, K, dtype, layout).item()) == 0
+    rm = _rand_meta(7, M, K)
+    _, erm = in_layout(ov, rm, dtype, layout)
+    Rt = torch.from_numpy(np.ascontiguousarray(erm).view(np.int32)).to(DEV)
+    for _ in range(2):
+        assert int(pkg.validate_meta(Rt, M, K, dtype, layout).item()) == oracle.count_invalid(rm, K)
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
