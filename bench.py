@@ -77,10 +77,23 @@ def load_traffic(name, kernel_src_hash):
     return t.get("gemm_bytes_per_launch")
 
 
+def cpu_model():
+    """The host CPU's model name (first entry of /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, rows, max_threads=16):
     """Time the oracle (as it stands) on `rows` rows of the workload on the
     host cores: prune+compress of those rows of A and those rows of the
-    product (full N and K)."""
+    product (full N and K).  One row block per thread, at most `max_threads`
+    threads (the CPU share that goes with one GPU on the GPU hosts)."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -88,10 +101,10 @@ def cpu_baseline(w, rows, max_threads=16):
     import oracle
     oracle.build(force=False)
     try:
-        cores = len(os.sched_getaffinity(0))
+        affinity = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count() or 1
-    threads = max(1, min(cores, max_threads, rows))
+        affinity = os.cpu_count() or 1
+    threads = max(1, min(affinity, max_threads, rows))
     A = np.ascontiguousarray(w.A[:rows])
     bounds = np.linspace(0, rows, threads + 1).astype(int)
     t0 = time.perf_counter()
@@ -113,9 +126,67 @@ def cpu_baseline(w, rows, max_threads=16):
         "kind": "oracle",
         "sample": f"{rows} of {w.M} rows: prune+compress of those rows of A and those rows of the product "
                   f"(full N={w.N}, K={w.K}); fp64/int64 plain C, one row block per thread",
+        "threads_used": threads,
+        "host_cpu_count": os.cpu_count(),
+        "affinity_cpu_count": affinity,
+        "cpu_model": cpu_model(),
         "compress_s": round(t1 - t0, 3),
         "product_s": round(t2 - t1, 3),
     }
+
+
+def measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream, rot_bytes=2 << 30):
+    """Kernels on data that is not in any cache.  Each call works on its own
+    copy of its inputs (and outputs), rotating over at least `rot_bytes` of
+    copies, so that by the time a copy is used again more than the 256 MB
+    Infinity Cache has been streamed since; one untimed pass over the
+    rotation, then one pass timed between two HIP events on the launch
+    stream (back-to-back launches: the launch overhead is hidden, as in a
+    batch).  compress: copies of A, A_vals and meta; gemm: copies of A_vals
+    and meta (and of B when it is larger than 1 MiB; a small-N B is the
+    activations, which a caller has just written)."""
+    import torch
+    sh = stream.cuda_stream
+
+    def rotate(tensors, bytes_each, fn):
+        n = max(2, -(-rot_bytes // max(1, bytes_each)))
+        copies = [[t.clone() for t in tensors] for _ in range(n)]
+        torch.cuda.synchronize()
+        for c in copies:
+            fn(*c)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for c in copies:
+            fn(*c)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / n * 1e3
+        del copies
+        torch.cuda.empty_cache()
+        return us, n
+
+    def check(st, what):
+        if st:
+            raise pkg.Sp24Error(st, what)
+
+    def comp(a, v, m):
+        check(pkg.sp24_prune_compress(a.data_ptr(), v.data_ptr(), m.data_ptr(), w.M, w.K, w.a_type, layout, sh),
+              "sp24_prune_compress")
+
+    cb = vals.numel() * vals.element_size() + meta.numel() * meta.element_size()
+    ab = A.numel() * A.element_size()
+    comp_us, nc = rotate([A, vals, meta], ab + cb, comp)
+    big_b = B.numel() * B.element_size() > (1 << 20)
+
+    def gem(v, m, *rest):
+        b = rest[0] if big_b else B
+        check(pkg.sp24_gemm(v.data_ptr(), m.data_ptr(), w.a_type, layout, b.data_ptr(), w.b_type, b_layout,
+                            C.data_ptr(), w.M, w.N, w.K, w.alpha, w.beta, None, 0, sh), "sp24_gemm")
+
+    gin = [vals, meta] + ([B] if big_b else [])
+    gbytes = sum(t.numel() * t.element_size() for t in gin)
+    gemm_us, ng = rotate(gin, gbytes, gem)
+    return comp_us, nc, gemm_us, ng
 
 
 def measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream, launches=20):
@@ -182,6 +253,8 @@ def main():
                     help="how B is stored: K x N (kn) or transposed, N x K (nk, e.g. activations)")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the oracle sample (default: sized to ~15 s)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache measurement (compress and gemm rotating over 2 GiB of input copies)")
     ap.add_argument("--next-rows", action="store_true",
                     help="also time the adjacent calls (decompress, validate_meta, 16-bit output with bias) "
                          "after the timed steps and add them to the line as next_rows")
@@ -292,6 +365,7 @@ def main():
         gemm()
     torch.cuda.synchronize()
     next_rows = measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream) if args.next_rows else None
+    cold = None if args.no_cold else measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream)
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     flop = 2.0 * w.M * w.N * w.K
@@ -347,6 +421,20 @@ def main():
         "roofline": roof,
         "kernel_src_hash": khash,
     }
+    if cold is not None:
+        c_us, nc, g_us, ng = cold
+        res["cold"] = {
+            "note": "each launch on its own copy of its inputs, rotating over >= 2 GiB of copies; "
+                    "back-to-back launches between two HIP events",
+            "compress": {"us": round(c_us, 2), "copies": nc, "bytes": comp_bytes,
+                         "GB/s": round(comp_bytes / c_us / 1e3, 1),
+                         "frac_hbm": round(comp_bytes / c_us / 1e3 / PEAK_HBM_GBPS, 4)},
+            "gemm": {"us": round(g_us, 2), "copies": ng, "bytes": gemm_bytes,
+                     "GB/s": round(gemm_bytes / g_us / 1e3, 1),
+                     "frac_hbm": round(gemm_bytes / g_us / 1e3 / PEAK_HBM_GBPS, 4),
+                     "TFLOP/s": round(flop / g_us / 1e6, 1),
+                     "frac_sparse_peak": round(flop / g_us / 1e6 / PEAK_SPARSE_TFLOPS[label], 4)},
+        }
     if next_rows is not None:
         res["next_rows"] = next_rows
     if not args.no_cpu:

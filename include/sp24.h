@@ -152,8 +152,23 @@ int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, 
  * value is multiplied with the row of B its position code selects, and the
  * products accumulate into D ("CDNA and CDNA2 sparse MFMA builtins", section
  * "Structured sparsity (4:2 pattern)"; the ISA page for
- * v_smfmac_f32_32x32x32_bf8_bf8, section "Semantics").  Products of the
- * supported inputs are exact in fp32; sums are fp32 (exact int32 for int8).
+ * v_smfmac_f32_32x32x32_bf8_bf8, section "Semantics").  Accumulation is
+ * fp32 (exact int32 for int8).  Measured behaviour of the matrix units on
+ * gfx950, which the parity tests pin:
+ *   - every single product of two fp16, bf16, fp8 or bf8 values (subnormals
+ *     included) is formed exactly and rounded to fp32 once; overflow gives
+ *     +-Inf, NaN inputs give NaN;
+ *   - fp32 results below 2^-126 (reachable from bf16 inputs only) land on
+ *     the denormal grid within one step (2^-149) of the exact value;
+ *   - for 8-bit float inputs, the products of each aligned run of 8
+ *     compressed elements (16 dense columns) are summed on a grid set by
+ *     the largest of them: with e the binary exponent of that largest
+ *     |product|, bits below 2^(e-13) are dropped.  On the N(0,1)-like data
+ *     of the configured workloads the product stays within
+ *     1e-4 * sum|a*b| + 1e-6 of the exact value; inputs whose products in
+ *     one run differ by 2^14 or more in magnitude can exceed that by up to
+ *     7 * 2^-13 of the run's largest product.  16-bit inputs meet the
+ *     1e-4 bound on any finite inputs whose exact sums stay in fp32 range.
  *
  *   A_vals, meta  compressed A in `layout`, as produced by
  *                 sp24_prune_compress (or any caller-built data in the same

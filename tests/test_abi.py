@@ -150,8 +150,8 @@ def test_gemm_ex_argument_errors(L):
     # misaligned bias, bias overlapping C
     assert g(F16, F16, F16, bias + 4, M=64) == 3
     assert g(F16, F16, F16, C + 64 * 64, M=64) == 1        # bias is the last bytes of a 64x64 fp16 C
-    # C of a 16-bit output is half the bytes: a bias right after it does not overlap
-    assert g(F16, F16, F16, C + 64 * 64 * 2, M=0) == 0
+    # (a bias right after a 16-bit C, which does not overlap it, is checked on
+    # the GPU with real adjacent buffers: test_gpu_parity.py)
 
 
 def test_decompress_and_validate_argument_errors(L):
