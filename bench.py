@@ -135,7 +135,52 @@ def cpu_baseline(w, rows, max_threads=16):
     }
 
 
-def measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream, rot_bytes=2 << 30):
+def compress_launch_shape(M, K, es, layout):
+    """(workgroups, threads) of the compress kernel the library launches."""
+    if layout == 1:  # K-blocked
+        nblk, row_tiles = -(-K // (64 if es == 2 else 128)), -(-M // 128)
+        if es == 2:
+            nb = 2 if row_tiles * (-(-nblk // 2)) >= 1024 else 1
+            return row_tiles * (-(-nblk // nb)), 256
+        return row_tiles * nblk, 512
+    return -(-(M * K * es // 16) // 1024), 256
+
+
+def stream_floor(pkg, read_bytes, write_bytes, workgroups, threads, stream, rot_bytes=2 << 30):
+    """Microseconds per launch of sp24_calib_stream (a plain stream of the
+    same bytes with the same launch shape), on data that is not in any
+    cache: rotating over >= rot_bytes of buffers, one untimed pass, then one
+    pass of back-to-back launches between two HIP events."""
+    import torch
+    read_bytes, write_bytes = -(-read_bytes // 16) * 16, -(-write_bytes // 16) * 16
+    n = max(2, -(-rot_bytes // (read_bytes + write_bytes)))
+    src = [torch.empty(read_bytes, dtype=torch.uint8, device="cuda:0") for _ in range(n)]
+    dst = [torch.empty(max(write_bytes, 16), dtype=torch.uint8, device="cuda:0") for _ in range(n)]
+    sink = torch.zeros(workgroups, dtype=torch.int32, device="cuda:0")
+    sh = stream.cuda_stream
+
+    def one(i):
+        st = pkg.sp24_calib_stream(src[i].data_ptr(), read_bytes, dst[i].data_ptr(), write_bytes, sink.data_ptr(),
+                                   workgroups, threads, sh)
+        if st:
+            raise pkg.Sp24Error(st, "sp24_calib_stream")
+
+    for i in range(n):
+        one(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        one(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    del src, dst
+    torch.cuda.empty_cache()
+    return us
+
+
+def measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream, ws, rot_bytes=2 << 30):
     """Kernels on data that is not in any cache.  Each call works on its own
     copy of its inputs (and outputs), rotating over at least `rot_bytes` of
     copies, so that by the time a copy is used again more than the 256 MB
@@ -181,7 +226,8 @@ def measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream, rot_byte
     def gem(v, m, *rest):
         b = rest[0] if big_b else B
         check(pkg.sp24_gemm(v.data_ptr(), m.data_ptr(), w.a_type, layout, b.data_ptr(), w.b_type, b_layout,
-                            C.data_ptr(), w.M, w.N, w.K, w.alpha, w.beta, None, 0, sh), "sp24_gemm")
+                            C.data_ptr(), w.M, w.N, w.K, w.alpha, w.beta, ws.data_ptr(), ws.numel(), sh),
+              "sp24_gemm")
 
     gin = [vals, meta] + ([B] if big_b else [])
     gbytes = sum(t.numel() * t.element_size() for t in gin)
@@ -189,7 +235,7 @@ def measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream, rot_byte
     return comp_us, nc, gemm_us, ng
 
 
-def measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream, launches=20):
+def measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream, ws, launches=20):
     """The calls adjacent to the hot path, each timed over back-to-back
     launches between two HIP events on the launch stream: sp24_decompress
     (bytes: values + metadata + dense A), sp24_validate_meta (bytes: metadata)
@@ -233,7 +279,8 @@ def measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream, launches=
         bias = torch.ones(w.N, dtype=torch.float32, device="cuda:0")
         us = timed(lambda: check(pkg.sp24_gemm_ex(vals.data_ptr(), meta.data_ptr(), w.a_type, layout, B.data_ptr(),
                                                   w.b_type, b_layout, D16.data_ptr(), wl.F16, bias.data_ptr(), w.M,
-                                                  w.N, w.K, 1.0, 0.0, None, 0, sh), "sp24_gemm_ex"), 5)
+                                                  w.N, w.K, 1.0, 0.0, ws.data_ptr(), ws.numel(), sh),
+                                 "sp24_gemm_ex"), 5)
         tf = 2.0 * w.M * w.N * w.K / (us * 1e-6) / 1e12
         out["gemm_ex_f16_out_bias"] = {"us": round(us, 1), "TFLOP/s": round(tf, 1)}
     return out
@@ -310,6 +357,10 @@ def main():
     meta = torch.empty(mshape, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    # small-N products split K over workgroups and need a workspace whose
+    # counters start at zero (the library leaves them at zero)
+    ws_bytes = pkg.sp24_gemm_workspace_bytes(w.M, w.N, w.K, w.a_type, w.b_type)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     def compress():
         st = pkg.sp24_prune_compress(A.data_ptr(), vals.data_ptr(), meta.data_ptr(), w.M, w.K, w.a_type, layout,
@@ -319,7 +370,7 @@ def main():
 
     def gemm():
         st = pkg.sp24_gemm(vals.data_ptr(), meta.data_ptr(), w.a_type, layout, B.data_ptr(), w.b_type, b_layout,
-                           C.data_ptr(), w.M, w.N, w.K, w.alpha, w.beta, None, 0, sh)
+                           C.data_ptr(), w.M, w.N, w.K, w.alpha, w.beta, ws.data_ptr(), ws_bytes, sh)
         if st:
             raise pkg.Sp24Error(st, "sp24_gemm")
 
@@ -364,8 +415,8 @@ def main():
     for _ in range(args.gemm_only_launches):
         gemm()
     torch.cuda.synchronize()
-    next_rows = measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream) if args.next_rows else None
-    cold = None if args.no_cold else measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream)
+    next_rows = measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream, ws) if args.next_rows else None
+    cold = None if args.no_cold else measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream, ws)
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     flop = 2.0 * w.M * w.N * w.K
@@ -423,18 +474,33 @@ def main():
     }
     if cold is not None:
         c_us, nc, g_us, ng = cold
+        cwg, cth = compress_launch_shape(w.M, w.K, es_a, layout)
+        floor_c = stream_floor(pkg, es_a * w.M * w.K, cbytes, cwg, cth, stream)
+        floor_g = None
+        if hbm_bound:  # the small-N product: one 16-row tile per 512-thread workgroup
+            floor_g = stream_floor(pkg, cbytes + es_b * w.K * w.N, 4 * w.M * w.N * (2 if w.beta != 0.0 else 1),
+                                   -(-w.M // 16), 512, stream)
         res["cold"] = {
             "note": "each launch on its own copy of its inputs, rotating over >= 2 GiB of copies; "
                     "back-to-back launches between two HIP events",
             "compress": {"us": round(c_us, 2), "copies": nc, "bytes": comp_bytes,
                          "GB/s": round(comp_bytes / c_us / 1e3, 1),
-                         "frac_hbm": round(comp_bytes / c_us / 1e3 / PEAK_HBM_GBPS, 4)},
+                         "frac_hbm": round(comp_bytes / c_us / 1e3 / PEAK_HBM_GBPS, 4),
+                         "stream_floor_us": round(floor_c, 2),
+                         "stream_floor_GB/s": round(comp_bytes / floor_c / 1e3, 1),
+                         "frac_of_floor": round(floor_c / c_us, 4),
+                         "floor_launch": [cwg, cth]},
             "gemm": {"us": round(g_us, 2), "copies": ng, "bytes": gemm_bytes,
                      "GB/s": round(gemm_bytes / g_us / 1e3, 1),
                      "frac_hbm": round(gemm_bytes / g_us / 1e3 / PEAK_HBM_GBPS, 4),
                      "TFLOP/s": round(flop / g_us / 1e6, 1),
                      "frac_sparse_peak": round(flop / g_us / 1e6 / PEAK_SPARSE_TFLOPS[label], 4)},
         }
+        if floor_g is not None:
+            res["cold"]["gemm"].update({"stream_floor_us": round(floor_g, 2),
+                                        "stream_floor_GB/s": round(gemm_bytes / floor_g / 1e3, 1),
+                                        "frac_of_floor": round(floor_g / g_us, 4),
+                                        "floor_launch": [-(-w.M // 16), 512]})
     if next_rows is not None:
         res["next_rows"] = next_rows
     if not args.no_cpu:

@@ -59,6 +59,8 @@ def lib():
         L.sp24_status_string.restype = ctypes.c_char_p
         L.sp24_version.argtypes = []
         L.sp24_version.restype = I
+        L.sp24_calib_stream.argtypes = [P, ctypes.c_uint64, P, ctypes.c_uint64, P, I, I, P]
+        L.sp24_calib_stream.restype = I
         _lib = L
     return _lib
 
@@ -107,6 +109,12 @@ def sp24_validate_meta(meta: int, M: int, K: int, dtype: int, layout: int, bad_g
 
 def sp24_status_string(status: int) -> str:
     return lib().sp24_status_string(status).decode()
+
+
+def sp24_calib_stream(src: int, read_bytes: int, dst: int, write_bytes: int, sink: int, workgroups: int,
+                      threads: int, stream) -> int:
+    """Measurement aid (include/sp24_calib.h): a plain HBM stream."""
+    return lib().sp24_calib_stream(src, read_bytes, dst, write_bytes, sink, workgroups, threads, stream)
 
 
 def sp24_version() -> int:
@@ -176,7 +184,8 @@ def prune_compress(A, dtype: int | None = None, layout: int = SP24_LAYOUT_KBLOCK
 
 
 def gemm(A_vals, meta, B, C=None, alpha: float = 1.0, beta: float = 0.0, a_type: int | None = None,
-         b_type: int | None = None, layout: int | None = None, stream=None, out_dtype=None, bias=None):
+         b_type: int | None = None, layout: int | None = None, stream=None, out_dtype=None, bias=None,
+         workspace=None):
     """D = alpha * expand(A_vals, meta) @ B + beta * C (+ bias), written into C
     (allocated, uninitialised, when C is None and beta == 0).  ``layout``
     defaults to what the tensors' rank says: 2-D = ROW, 3-D = KBLOCK.
@@ -185,7 +194,10 @@ def gemm(A_vals, meta, B, C=None, alpha: float = 1.0, beta: float = 0.0, a_type:
     ``out_dtype`` (torch.float32 by default, or float16 / bfloat16; int32 for
     int8 inputs) is the type of C / D, taken from C when it is given.
     ``bias``: optional length-N float32 tensor added to every row (calls
-    sp24_gemm_ex).  Returns C."""
+    sp24_gemm_ex).  ``workspace``: optional uint8 device tensor of at least
+    sp24_gemm_workspace_bytes() bytes, zero-filled before its first use (the
+    library leaves its counters at zero); allocated per call when needed and
+    not given.  Returns C."""
     import torch
     if a_type is None:
         a_type = dtype_code(A_vals.dtype)
@@ -223,14 +235,22 @@ def gemm(A_vals, meta, B, C=None, alpha: float = 1.0, beta: float = 0.0, a_type:
             raise ValueError("A_vals, meta and C must be contiguous")
     if bias is not None and (bias.dtype != torch.float32 or not bias.is_contiguous() or bias.numel() != N):
         raise ValueError("bias must be a contiguous float32 tensor of N values")
+    # the small-N product splits K over workgroups and combines their partial
+    # tiles through a workspace whose counters start at zero (and are left
+    # at zero): a fresh zero-filled buffer per call here
+    ws_bytes = sp24_gemm_workspace_bytes(M, N, K, a_type, b_type)
+    if workspace is None and ws_bytes:
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=B.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if bias is None and c_type == (SP24_I32 if is_int else SP24_F32):
         st = sp24_gemm(A_vals.data_ptr(), meta.data_ptr(), a_type, layout, B.data_ptr(), b_type, b_layout,
-                       C.data_ptr(), M, N, K, float(alpha), float(beta), None, 0, _stream(stream))
+                       C.data_ptr(), M, N, K, float(alpha), float(beta), ws_ptr, ws_len, _stream(stream))
         what = "sp24_gemm"
     else:
         st = sp24_gemm_ex(A_vals.data_ptr(), meta.data_ptr(), a_type, layout, B.data_ptr(), b_type, b_layout,
                           C.data_ptr(), c_type, None if bias is None else bias.data_ptr(), M, N, K, float(alpha),
-                          float(beta), None, 0, _stream(stream))
+                          float(beta), ws_ptr, ws_len, _stream(stream))
         what = "sp24_gemm_ex"
     if st != SP24_OK:
         raise Sp24Error(st, what)

@@ -747,10 +747,12 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
   };
 
   // Chunks of D local steps: all B slices first (direct-to-LDS), then all A
-  // fragments and idx words (register loads the compiler sees and waits for
-  // itself, exactly, since nothing it cannot see is issued after them).
-  // Loads complete in order, so vmcnt(2D) means every B slice of the chunk
-  // has landed.
+  // fragments and idx words (register loads the compiler sees), then one
+  // wait for everything.  (A wait that counts only the register loads, 2D of
+  // them in the source, is not safe: the compiler may merge identical loads,
+  // e.g. those of two steps past the wave's last one in the row-major
+  // layout, which read the same out-of-range offset, so their number is not
+  // fixed by the source.)
   for (int j0 = 0; j0 < nw; j0 += D) {
     i32x4 ar[D];
     int ir[D];
@@ -763,7 +765,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
 #pragma unroll
     for (int u = 0; u < D; ++u) load_a(j0 + u, ar[u], ir[u]);
     __builtin_amdgcn_sched_barrier(0);
-    waitcnt<2 * D>();
+    waitcnt<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     // (every slot, also past the wave's last step: those read nothing, their

@@ -20,17 +20,32 @@ def L():
 
 
 def header_functions():
-    text = open(os.path.join(ROOT, "include", "sp24.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sp24_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(sp24_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) >= 7, names
+    assert len(names) >= 8 and "sp24_calib_stream" in names, names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in sp24.h but not exported"
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def test_calib_stream_argument_errors(L):
+    f = L.sp24_calib_stream
+    assert f(0, 64, P, 32, P, 4, 256, None) == 1           # null source
+    assert f(P, 64, P, 96, P, 4, 256, None) == 1           # writes more than it reads
+    assert f(P, 60, P, 32, P, 4, 256, None) == 1           # not a multiple of 16
+    assert f(P, 64, P, 32, P, 0, 256, None) == 1           # no workgroups
+    assert f(P, 64, P, 32, P, 4, 96, None) == 1            # threads not a multiple of 64
+    assert f(P + 8, 64, P, 32, P, 4, 256, None) == 3       # misaligned
+    assert f(P, 0, 0, 0, P, 4, 256, None) == 0             # nothing to do, nothing launched
 
 
 def test_size_queries(L):
