@@ -18,16 +18,21 @@ extern "C" {
 
 /*
  * sp24_calib_stream -- reads read_bytes from src in 16-byte pieces and
- * copies the first write_bytes of them to dst (write_bytes <= read_bytes),
- * with `workgroups` workgroups of `threads` threads (a multiple of 64, at
- * most 1024) walking the pieces in a grid-stride loop, four 16-byte loads
- * in flight per thread.  The xor of everything read by workgroup w is
- * written to sink[w], so no load can be left out by the compiler.
+ * copies the first write_bytes of them to dst (write_bytes <= read_bytes)
+ * with workgroups of `threads` threads (a multiple of 64, at most 1024):
+ *   workgroups > 0: that many workgroups walk the pieces in a grid-stride
+ *                   loop, four 16-byte loads in flight per thread;
+ *   workgroups == 0: one pass, ceil(read_bytes / (128 * threads))
+ *                   workgroups, each thread with eight 16-byte loads in
+ *                   flight at a stride of the block size, then its stores
+ *                   (the shape of the library's compress kernels).
+ * The xor of everything read by workgroup w is xor-ed into sink[w], so no
+ * load can be left out by the compiler.
  *
  *   src, dst  DEVICE pointers, 16-byte aligned; read_bytes and write_bytes
  *             multiples of 16.  dst may be NULL when write_bytes == 0.
- *   sink      DEVICE pointer to `workgroups` uint32 values.
- * Errors: SP24_ERR_INVALID_VALUE (sizes, null pointers, workgroups < 1,
+ *   sink      DEVICE pointer to one uint32 per workgroup launched.
+ * Errors: SP24_ERR_INVALID_VALUE (sizes, null pointers, workgroups < 0,
  * threads not a multiple of 64 in 64..1024), SP24_ERR_MISALIGNED,
  * SP24_ERR_LAUNCH.  Enqueues on `stream` only.
  */

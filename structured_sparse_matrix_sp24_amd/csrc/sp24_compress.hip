@@ -184,11 +184,19 @@ constexpr int kKbRowsPerTile = 128;
 
 // Launch shape, measured on cold data over 2048..16384-row, 4096..16384-
 // column A: 16-bit types take NB = 2 blocks per workgroup (each row's 256
-// contiguous bytes read by 16 lanes) with 256 threads when that still gives
+// contiguous bytes read by 16 lanes) with 512 threads when that still gives
 // at least 1024 workgroups, else NB = 1; 8-bit types take NB = 1 with 512
-// threads.  8192 x 8192: fp16 36.4 us, int8 22.3 us.
+// threads.  Cold inputs, back to back: fp16 8192 x 8192 40 us (41.5 us with
+// 256 threads), fp16 4096 x 4096 10.6 us (11.1), int8 8192 x 8192 24 us.
+// Measured and not kept: NB = 4 or 8 (with the values staged in LDS so they
+// still leave as 8 KiB runs: 40.8 and 43.8 us); consecutive workgroups on
+// consecutive row tiles of one block group instead of consecutive block
+// groups of one row tile (47 to 52 us); one workgroup per row segment,
+// reading rows linearly and scattering values and codes (57 us).  The
+// row-major layout's kernel, whose reads and writes are both one linear
+// stream, takes 36.3 us for the same A.
 constexpr int64_t kKbMinWorkgroups = 1024;
-constexpr int kKbBlocks16 = 2, kKbThreads16 = 256, kKbThreads8 = 512;
+constexpr int kKbBlocks16 = 2, kKbThreads16 = 512, kKbThreads8 = 512;
 
 template <int ES, bool INT, int NB, int T>
 __global__ __launch_bounds__(T) void prune_compress_kblock_kernel(const char* __restrict__ A, char* __restrict__ vals,

@@ -555,17 +555,25 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
 // in L2).  A workgroup of 8 waves owns one 16-row tile and all N columns; the
 // waves take the k-steps round-robin (wave w: steps w, w+8, ...).  A wave
 // works through its steps in chunks of D, all of whose loads are in flight at
-// once: the B slices (KS rows x N; for B stored N x K, N rows of the step's
-// 128 bytes with chunk c of row n at c ^ swzBT(n)) go into the wave's LDS
-// ring by direct-to-LDS loads issued through inline assembly, then the A
-// fragments (16 bytes per lane) and idx words (4 bytes) straight into
-// registers.  Loads past the wave's last step read nothing, so every step
-// issues the same number of loads.  The 8 partial tiles are summed on chip
-// in a fixed order (deterministic).
+// once: the A fragments (16 bytes per lane) and idx words (4 bytes) straight
+// into registers, then the B slices (KS rows x N; for B stored N x K, N rows
+// of the step's 128 bytes with chunk c of row n at c ^ swzBT(n)) into the
+// wave's LDS ring by direct-to-LDS loads issued through inline assembly.
+// Loads past the wave's last step read nothing, so every step issues the
+// same number of loads.  The 8 partial tiles are summed on chip in a fixed
+// order (deterministic).
 //   D = 16 KiB / B-slice bytes: 8 (N <= 16), 4 (N <= 32), 2 (N <= 64), so
 //   the ring holds 128 KiB of B per workgroup.  (bf16 4096 x 16 x 4096:
 //   with A and idx staged in LDS as well the ring could hold only 5 steps,
 //   7.6 us per launch.)
+// What bounds it: every workgroup (one per CU at 4096 rows) reads all of B,
+// 128 KiB from L2 for its 72 KiB of A and codes, so each CU's vector-memory
+// path moves about 3x the bytes its share of HBM traffic needs.  Splitting
+// K over workgroups cuts that, but the partial tiles then have to be
+// combined across XCDs, whose L2s are not coherent: with system-scope
+// stores, loads and a counter the measured chain of round trips made the
+// product 2x slower (17.5 against 8.6 us cold), and with device-scope
+// fences (which write back and invalidate whole L2s) 15x slower.
 // ----------------------------------------------------------------------------
 constexpr int kSmallWaves = 8;
 constexpr int kSmallRingBytes = 16384;  // per wave
@@ -746,9 +754,10 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
     }
   };
 
-  // Chunks of D local steps: all B slices first (direct-to-LDS), then all A
-  // fragments and idx words (register loads the compiler sees), then one
-  // wait for everything.  (A wait that counts only the register loads, 2D of
+  // Chunks of D local steps: first the A fragments and idx words (register
+  // loads the compiler sees; they come from HBM, so they go first: 3 % faster
+  // than B first), then all B slices (direct-to-LDS, from L2), then one wait
+  // for everything.  (A wait that counts only the register loads, 2D of
   // them in the source, is not safe: the compiler may merge identical loads,
   // e.g. those of two steps past the wave's last one in the row-major
   // layout, which read the same out-of-range offset, so their number is not
@@ -759,11 +768,11 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < D; ++u) issue_b(j0 + u, u);
+    for (int u = 0; u < D; ++u) load_a(j0 + u, ar[u], ir[u]);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < D; ++u) load_a(j0 + u, ar[u], ir[u]);
+    for (int u = 0; u < D; ++u) issue_b(j0 + u, u);
     __builtin_amdgcn_sched_barrier(0);
     waitcnt<0>();
     asm volatile("" ::: "memory");

@@ -42,7 +42,7 @@ def test_calib_stream_argument_errors(L):
     assert f(0, 64, P, 32, P, 4, 256, None) == 1           # null source
     assert f(P, 64, P, 96, P, 4, 256, None) == 1           # writes more than it reads
     assert f(P, 60, P, 32, P, 4, 256, None) == 1           # not a multiple of 16
-    assert f(P, 64, P, 32, P, 0, 256, None) == 1           # no workgroups
+    assert f(P, 64, P, 32, P, -1, 256, None) == 1          # negative workgroup count
     assert f(P, 64, P, 32, P, 4, 96, None) == 1            # threads not a multiple of 64
     assert f(P + 8, 64, P, 32, P, 4, 256, None) == 3       # misaligned
     assert f(P, 0, 0, 0, P, 4, 256, None) == 0             # nothing to do, nothing launched
