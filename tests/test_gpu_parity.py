@@ -9,10 +9,11 @@ instructions at K = 16384, far inside 1e-4.  The matrix units' own
 rounding inside an 8-bit instruction, which matters only for inputs of
 widely different magnitudes, is pinned in test_gpu_edge_values.py.)
 
-Small cases are compared element by element over the whole output; the full
-benchmark-size workloads are compared on sampled outputs (random points plus
-the first and last rows and columns), in the same launch configuration the
-benchmark times (K-blocked layout).  The oracle produces the row-major
+Small cases are compared element by element over the whole output.  The
+full benchmark-size workloads are compared at every output
+(test_workload_full_output) and, in the other layouts and repeated runs, on
+sampled outputs (random points plus the first and last rows and columns), in
+the same launch configuration the benchmark times (K-blocked layout).  The oracle produces the row-major
 compressed layout; K-blocked inputs and expected outputs are the same data
 moved by tests/layouts.py.
 """
@@ -619,18 +620,20 @@ def oracle_full_threaded(vals, meta, w, max_threads=16):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["f16_8192", "i8_8192"])
+@pytest.mark.parametrize("name", ["f16_8192", "i8_8192", "fp8_bf8_8192x16384", "bf8_bf8_8192x16384", "f16_4096",
+                                  "bf16_linear_n4096", "bf16_linear_n16"])
 def test_workload_full_output(pkg, name):
-    """The benchmark's fp16 and int8 8192^3 products, compared with the oracle
-    at every one of the 67 million outputs (not sampled), in the launch
-    configuration the benchmark times (K-blocked A from the GPU compressor,
-    B stored K x N)."""
+    """Every configured workload's product compared with the oracle at every
+    output (not sampled), in the launch configuration the benchmark times
+    (K-blocked A from the GPU compressor, B stored K x N; C and beta as the
+    workload has them)."""
     _say(f"workload {name} full output: generating inputs")
     w = wl.make(name)
     A = to_dev(w.A, w.a_type)
     vals_d, meta_d = pkg.prune_compress(A, w.a_type, KBLOCK)
     del A
-    D = pkg.gemm(vals_d, meta_d, to_dev(w.B, w.b_type), None, alpha=w.alpha, beta=w.beta, a_type=w.a_type,
+    C = None if w.C is None else torch.from_numpy(w.C).to(DEV)
+    D = pkg.gemm(vals_d, meta_d, to_dev(w.B, w.b_type), C, alpha=w.alpha, beta=w.beta, a_type=w.a_type,
                  b_type=w.b_type)
     torch.cuda.synchronize()
     got = D.cpu().numpy()
