@@ -179,7 +179,8 @@ int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, 
  *                 N x K (SP24_B_NK), as `b_layout` says.
  *   C             in/out: M x N float32 (int32 for int8 x int8).  Not read
  *                 when beta == 0 (NaN there does not propagate).
- *   M, N, K       >= 0, K % 32 == 0, N * sizeof(b_type) % 16 == 0,
+ *   M, N, K       >= 0, K % 32 == 0, N % 8 == 0 (and, for 8-bit B stored
+ *                 K x N with N > 64, N % 16 == 0),
  *                 N * sizeof(b_type) <= 16 MiB - 2 (so 128 rows of B stay
  *                 below 2 GiB), for SP24_B_NK 256 * K * sizeof(b_type) <
  *                 2 GiB and, for the ROW layout, 256 * K/2 * sizeof(a_type)
@@ -188,9 +189,9 @@ int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, 
  *   alpha, beta   float scalars.  For int8: alpha must be 1, beta 0 or 1.
  *   workspace     may be NULL when sp24_gemm_workspace_bytes() == 0.
  * Errors: INVALID_VALUE (shape, null pointer, C overlapping an input,
- * workspace too small), UNSUPPORTED (type pair, int8 alpha/beta, N*size not a
- * multiple of 16 bytes, N or K past the limits above, unknown layout or
- * b_layout), MISALIGNED, LAUNCH.
+ * workspace too small), UNSUPPORTED (type pair, int8 alpha/beta, N not a
+ * multiple of 8 (of 16 for 8-bit B stored K x N with N > 64), N or K past
+ * the limits above, unknown layout or b_layout), MISALIGNED, LAUNCH.
  */
 int sp24_gemm(const void* A_vals, const uint32_t* meta, int a_type, int layout, const void* B, int b_type,
               int b_layout, void* C, int64_t M, int64_t N, int64_t K, float alpha, float beta, void* workspace,

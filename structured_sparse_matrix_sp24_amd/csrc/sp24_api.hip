@@ -120,7 +120,12 @@ int sp24_gemm_ex(const void* A_vals, const uint32_t* meta, int a_type, int layou
   if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
     return SP24_ERR_INVALID_VALUE;
   const int ea = esize(a_type), eb = esize(b_type);
-  if (((uint64_t)N * eb) % 16 != 0) return SP24_ERR_UNSUPPORTED;
+  // N % 8: 16-byte rows of a 16-bit output and of 16-bit B.  8-bit B stored
+  // K x N also needs 16-byte rows where the large-tile kernel (N > 64)
+  // stages it; the small-N kernel loads each k-step's rows of B as one
+  // contiguous run (128 * N bytes, a whole number of KiB).
+  if (N % 8 != 0) return SP24_ERR_UNSUPPORTED;
+  if (eb == 1 && b_layout == SP24_B_KN && N > 64 && N % 16 != 0) return SP24_ERR_UNSUPPORTED;
   // The kernels address one k-step of B (<= 128 rows) and, in the ROW layout,
   // the compressed rows of one 256-row tile with 32-bit offsets inside
   // buffer ranges below 2 GiB.

@@ -611,9 +611,8 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
   const int nw = nsteps > w ? (nsteps - w + kSmallWaves - 1) / kSmallWaves : 0;  // this wave's steps
   const int64_t rowA = (int64_t)K / 2 * ES, rowM = (int64_t)K / 8;
   const int64_t Mp = ((int64_t)M + 127) / 128 * 128;  // KBLOCK metadata rows per block
-  const int ldb = N * ES;                              // bytes per K x N row (multiple of 16)
+  const int ldb = N * ES;                              // bytes per K x N row (a multiple of 8)
   const int64_t ldbk = (int64_t)K * ES;                // bytes per N x K row
-  const int chunks_per_row = ldb >> 4;
   const int slice_instr = (KS * ldb) >> 10;            // 1 KiB per load (KS*ldb = 128*N is a multiple of 1 KiB)
   const int64_t btotal = (int64_t)K * ldb;
   const int t16 = (m0 & 127) >> 4;                     // KBLOCK: row tile of the tile inside its 128-row group
@@ -624,8 +623,8 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
   // fragment).  idx: the dword holding word ga of row m0+s (K-blocked: inside
   // the tile's 128-row group, for row tile t16; row-major: for 16-bit types
   // the dword holding the u16 word ga).  B: 1 KiB per load, lane l of load q
-  // -> chunk 64q + l of the slice (N x K: row n = 8q + l/8, chunk
-  // (l%8) ^ swzBT(n) of the step).
+  // -> chunk 64q + l of the slice, which is one contiguous run of KS rows
+  // in K x N (N x K: row n = 8q + l/8, chunk (l%8) ^ swzBT(n) of the step).
   const uint32_t offA = LAYOUT == SP24_LAYOUT_KBLOCK ? (uint32_t)(s * 64 + 16 * ga) : (uint32_t)(s * rowA + 16 * ga);
   uint32_t offM;
   if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK)
@@ -639,9 +638,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
       const int n = 8 * q + (l >> 3);
       offB[q] = (uint32_t)(n * ldbk + 16 * ((l & 7) ^ swzBT(n)));
     } else {
-      const int c = q * 64 + l;
-      const int brow = c / chunks_per_row, bc = c - brow * chunks_per_row;
-      offB[q] = (uint32_t)(brow * ldb + 16 * bc);
+      offB[q] = (uint32_t)(16 * (q * 64 + l));
     }
   }
   const int nfull = K / KS;

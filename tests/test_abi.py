@@ -114,8 +114,13 @@ def test_gemm_argument_errors(L):
         assert g(A, Mt, F16, B, E4, C, 64, 64, 64, 1.0, 0.0, None, 0, None) == 2
         assert g(A, Mt, I8, B, F16, C, 64, 64, 64, 1.0, 0.0, None, 0, None) == 2
         assert g(A, Mt, F16, B, F16, C, 64, 64, 48, 1.0, 0.0, None, 0, None) == 1   # K % 32
-        assert g(A, Mt, F16, B, F16, C, 64, 12, 64, 1.0, 0.0, None, 0, None) == 2   # N*2 % 16
-        assert g(A, Mt, E4, B, E5, C, 64, 24, 64, 1.0, 0.0, None, 0, None) == 2     # N*1 % 16
+        assert g(A, Mt, F16, B, F16, C, 64, 12, 64, 1.0, 0.0, None, 0, None) == 2   # N % 8
+        assert g(A, Mt, E4, B, E5, C, 64, 20, 64, 1.0, 0.0, None, 0, None) == 2     # N % 8
+        # 8-bit B stored K x N: N % 8 up to 64 (small-N kernel), N % 16 above
+        assert g(A, Mt, E4, B, E5, C, 64, 72, 64, 1.0, 0.0, None, 0, None) == 2
+        assert g(A, Mt, E4, B, E5, C, 0, 72, 64, 1.0, 0.0, None, 0, None, bl=L.SP24_B_NK) == 0
+        assert g(A, Mt, I8, B, I8, C, 0, 24, 64, 1.0, 0.0, None, 0, None) == 0
+        assert g(A, Mt, I8, B, I8, C, 0, 72, 64, 1.0, 0.0, None, 0, None) == 2
         assert g(A, Mt, I8, B, I8, C, 64, 64, 64, 2.0, 0.0, None, 0, None) == 2     # int8 alpha
         assert g(A, Mt, I8, B, I8, C, 64, 64, 64, 1.0, 0.5, None, 0, None) == 2     # int8 beta
         assert g(A, Mt, F16, B, F16, C + 4, 64, 64, 64, 1.0, 0.0, None, 0, None) == 3
