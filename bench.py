@@ -237,6 +237,43 @@ def measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream, ws, rot_
     return comp_us, nc, gemm_us, ng
 
 
+def mfma_ceiling(pkg, w, vals, meta, B, layout, stream, launches=10):
+    """TFLOP/s (dense-equivalent) of sp24_calib_mfma: the product's sparse
+    instructions for this type pair with their operands (taken from this
+    workload's compressed A, codes and B) held in registers, no memory
+    traffic.  One workgroup per CU and as many instructions per launch as the
+    product issues; back-to-back launches between two HIP events."""
+    import torch
+    from structured_sparse_matrix_sp24_amd import workloads as wl
+    kstep = 64 if wl.ESIZE[w.a_type] == 2 else 128
+    tiles = -(-w.M // 256) * -(-w.N // 256)
+    rounds = max(1, tiles * -(-w.K // kstep) // 256)
+    wgs = 256
+    sink = torch.zeros(wgs, dtype=torch.int32, device="cuda:0")
+    vb = pkg.sp24_values_bytes(w.M, w.K, w.a_type, layout)
+    mb = pkg.sp24_meta_bytes(w.M, w.K, w.a_type, layout)
+    bb = B.numel() * B.element_size()
+
+    def one():
+        st = pkg.sp24_calib_mfma(vals.data_ptr(), vb, meta.data_ptr(), mb, B.data_ptr(), bb, w.a_type, w.b_type,
+                                 rounds, wgs, sink.data_ptr(), stream.cuda_stream)
+        if st:
+            raise pkg.Sp24Error(st, "sp24_calib_mfma")
+
+    for _ in range(3):
+        one()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(launches):
+        one()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / launches * 1e3
+    flop = wgs * 8.0 * rounds * 32 * 2 * 16 * 16 * kstep
+    return us, flop / us / 1e6, rounds, wgs
+
+
 def measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream, ws, launches=20):
     """The calls adjacent to the hot path, each timed over back-to-back
     launches between two HIP events on the launch stream: sp24_decompress
@@ -304,6 +341,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache measurement (compress and gemm rotating over 2 GiB of input copies)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the matrix-core ceiling (sp24_calib_mfma) of the large-N products")
     ap.add_argument("--next-rows", action="store_true",
                     help="also time the adjacent calls (decompress, validate_meta, 16-bit output with bias) "
                          "after the timed steps and add them to the line as next_rows")
@@ -419,6 +458,7 @@ def main():
     torch.cuda.synchronize()
     next_rows = measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream, ws) if args.next_rows else None
     cold = None if args.no_cold else measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream, ws)
+    ceiling = None if (args.no_ceiling or w.N <= 64) else mfma_ceiling(pkg, w, vals, meta, B, layout, stream)
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     flop = 2.0 * w.M * w.N * w.K
@@ -508,6 +548,16 @@ def main():
                                         "stream_floor_GB/s": round(gemm_bytes / floor_g / 1e3, 1),
                                         "frac_of_floor": round(floor_g / g_us, 4),
                                         "floor_launch": shape_g})
+    if ceiling is not None:
+        c_us, c_tf, c_rounds, c_wgs = ceiling
+        res["mfma_ceiling"] = {
+            "note": "sp24_calib_mfma: the product's sparse instructions on this workload's operands held in "
+                    "registers, no memory traffic; as many instructions per launch as the product",
+            "us": round(c_us, 1), "TFLOP/s": round(c_tf, 1),
+            "frac_sparse_peak": round(c_tf / PEAK_SPARSE_TFLOPS[label], 4),
+            "gemm_frac_of_ceiling": round(gemm_tflops / c_tf, 4),
+            "launch": {"workgroups": c_wgs, "rounds": c_rounds},
+        }
     if next_rows is not None:
         res["next_rows"] = next_rows
     if not args.no_cpu:

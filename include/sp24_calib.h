@@ -1,10 +1,15 @@
 /*
- * sp24_calib.h -- measurement aid exported by libsp24 (not a step of the
- * 2:4 method): a plain HBM stream used to measure, on the machine at hand,
- * the rate a bandwidth-bound kernel of the library could at best reach for
- * the same bytes and the same launch shape.  The benchmark reports each
- * bandwidth-bound kernel against both this measured floor and the published
- * HBM peak.
+ * sp24_calib.h -- measurement aids exported by libsp24 (not steps of the
+ * 2:4 method):
+ *   - a plain HBM stream, to measure on the machine at hand the rate a
+ *     bandwidth-bound kernel of the library could at best reach for the
+ *     same bytes and the same launch shape;
+ *   - the product's sparse matrix-core instruction stream with its operands
+ *     held in registers, to measure the rate the matrix cores sustain on the
+ *     workload's own operand values (their power draw depends on the data,
+ *     and the clock on the power).
+ * The benchmark reports each kernel against both the measured figure and
+ * the published peak.
  */
 #ifndef SP24_CALIB_H
 #define SP24_CALIB_H
@@ -38,6 +43,36 @@ extern "C" {
  */
 int sp24_calib_stream(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes, uint32_t* sink,
                       int workgroups, int threads, void* stream);
+
+/*
+ * sp24_calib_mfma -- the instruction stream of sp24_gemm's large-tile main
+ * loop with no memory traffic.  Each of `workgroups` workgroups runs 8 waves
+ * (two per SIMD).  Wave v = 8 * workgroup + wave index loads, once, the
+ * operands of one k-step of a 128 x 64 wave tile:
+ *   8 A fragments:  bytes [8192 * (v % na), +8192) of a_vals, 16 per lane
+ *                   per fragment (na = a_bytes / 8192);
+ *   8 code words:   bytes [2048 * (v % nc), +2048) of codes, one 32-bit
+ *                   word per lane per fragment (nc = code_bytes / 2048);
+ *   4 B fragments:  bytes [8192 * (v % nb), +8192) of b, 32 per lane per
+ *                   fragment (nb = b_bytes / 8192);
+ * and then issues `rounds` times the 32 sparse instructions of one k-step of
+ * the (a_type, b_type) pair (16x16x64 for 16-bit types, 16x16x128 for 8-bit)
+ * into 32 accumulator tiles.  Dense-equivalent work per launch:
+ *   workgroups * 8 * rounds * 32 * 2 * 16 * 16 * (64 or 128) flop.
+ * Pass the product's own compressed A, its codes and B so the instructions
+ * multiply the workload's values; any bytes are accepted (code words are
+ * used as they are).  The xor of each wave's accumulator bits is xor-ed into
+ * sink[workgroup].
+ *
+ *   a_vals, codes, b   DEVICE pointers, 16-byte aligned, with at least 8192,
+ *                      2048 and 8192 bytes.
+ *   sink               DEVICE pointer to `workgroups` uint32 values.
+ * Errors: SP24_ERR_UNSUPPORTED (type pair), SP24_ERR_INVALID_VALUE (null
+ * pointer, too few bytes, rounds or workgroups < 1), SP24_ERR_MISALIGNED,
+ * SP24_ERR_LAUNCH.  Enqueues on `stream` only.
+ */
+int sp24_calib_mfma(const void* a_vals, uint64_t a_bytes, const uint32_t* codes, uint64_t code_bytes, const void* b,
+                    uint64_t b_bytes, int a_type, int b_type, int rounds, int workgroups, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

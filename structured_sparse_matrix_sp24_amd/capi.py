@@ -61,6 +61,9 @@ def lib():
         L.sp24_version.restype = I
         L.sp24_calib_stream.argtypes = [P, ctypes.c_uint64, P, ctypes.c_uint64, P, I, I, P]
         L.sp24_calib_stream.restype = I
+        U64 = ctypes.c_uint64
+        L.sp24_calib_mfma.argtypes = [P, U64, P, U64, P, U64, I, I, I, I, P, P]
+        L.sp24_calib_mfma.restype = I
         _lib = L
     return _lib
 
@@ -115,6 +118,14 @@ def sp24_calib_stream(src: int, read_bytes: int, dst: int, write_bytes: int, sin
                       threads: int, stream) -> int:
     """Measurement aid (include/sp24_calib.h): a plain HBM stream."""
     return lib().sp24_calib_stream(src, read_bytes, dst, write_bytes, sink, workgroups, threads, stream)
+
+
+def sp24_calib_mfma(a_vals: int, a_bytes: int, codes: int, code_bytes: int, b: int, b_bytes: int, a_type: int,
+                    b_type: int, rounds: int, workgroups: int, sink: int, stream) -> int:
+    """Measurement aid (include/sp24_calib.h): the product's sparse-MFMA
+    instruction stream with its operands in registers."""
+    return lib().sp24_calib_mfma(a_vals, a_bytes, codes, code_bytes, b, b_bytes, a_type, b_type, rounds, workgroups,
+                                 sink, stream)
 
 
 def sp24_version() -> int:

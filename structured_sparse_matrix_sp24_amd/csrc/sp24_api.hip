@@ -35,18 +35,7 @@ bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// Sparse-MFMA operation for an (A, B) type pair, or -1.
-int op_for(int a, int b) {
-  using namespace sp24;
-  if (a == SP24_F16 && b == SP24_F16) return OP_F16;
-  if (a == SP24_BF16 && b == SP24_BF16) return OP_BF16;
-  if (a == SP24_I8 && b == SP24_I8) return OP_I8;
-  if (a == SP24_FP8_E4M3 && b == SP24_FP8_E4M3) return OP_FP8_FP8;
-  if (a == SP24_FP8_E4M3 && b == SP24_BF8_E5M2) return OP_FP8_BF8;
-  if (a == SP24_BF8_E5M2 && b == SP24_FP8_E4M3) return OP_BF8_FP8;
-  if (a == SP24_BF8_E5M2 && b == SP24_BF8_E5M2) return OP_BF8_BF8;
-  return -1;
-}
+using sp24::op_for;
 
 constexpr int64_t kMaxDim = 0x7FFFFFFF;
 constexpr uint64_t kTileBytesMax = 0x7FFFFF00ull;

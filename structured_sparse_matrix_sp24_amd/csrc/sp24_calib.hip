@@ -1,7 +1,10 @@
-// sp24_calib_stream: a plain HBM stream (read, and copy a prefix of what was
-// read), used by the benchmark as the measured floor of the library's
-// bandwidth-bound kernels for the same bytes and launch shape.  Not part of
-// the 2:4 method.
+// Measurement aids, not steps of the 2:4 method:
+//   sp24_calib_stream: a plain HBM stream (read, and copy a prefix of what
+//     was read), the measured floor of the library's bandwidth-bound kernels
+//     for the same bytes and launch shape;
+//   sp24_calib_mfma: the product's sparse-MFMA instruction stream with its
+//     operands held in registers, the measured ceiling of the matrix cores on
+//     the workload's own operand values.
 #include "../../include/sp24_calib.h"
 #include "sp24_internal.hpp"
 
@@ -62,7 +65,93 @@ __global__ void calib_stream_once_kernel(const i32x4* __restrict__ src, int64_t 
   if ((threadIdx.x & 63) == 0) atomicXor(sink + blockIdx.x, acc);
 }
 
+// The product's matrix-core work with the memory side taken away.  Each
+// wave holds one k-step's operands of a 128 x 64 wave tile (8 A fragments
+// with their codes, 4 B fragments), loaded once, and then issues `rounds`
+// times the 32 instructions of a k-step in the product's order (each B
+// fragment against the 8 A fragments), into 8 x 4 accumulator tiles.  Eight
+// waves per workgroup, two per SIMD, as in the product; here both waves of a
+// SIMD issue instructions all the time.
+constexpr int kCalibWaves = 8;
+constexpr uint64_t kCalibAUnit = 8 * 1024, kCalibBUnit = 4 * 2048, kCalibCUnit = 8 * 64 * 4;
+
+template <int OP>
+__global__ __launch_bounds__(kCalibWaves * 64) void calib_mfma_kernel(const char* __restrict__ a, uint64_t na,
+                                                                      const char* __restrict__ codes, uint64_t nc,
+                                                                      const char* __restrict__ b, uint64_t nb,
+                                                                      int rounds, uint32_t* __restrict__ sink) {
+  const int l = threadIdx.x & 63;
+  const uint64_t gw = (uint64_t)blockIdx.x * kCalibWaves + (threadIdx.x >> 6);  // this wave's fragment set
+  const char* pa = a + (gw % na) * kCalibAUnit + 16 * l;
+  const char* pc = codes + (gw % nc) * kCalibCUnit + 4 * l;
+  const char* pb = b + (gw % nb) * kCalibBUnit + 32 * l;
+  i32x4 fa[8];
+  int idx[8];
+  i32x8 fb[4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    fa[t] = *(const i32x4*)(pa + t * 1024);
+    idx[t] = *(const int*)(pc + t * 256);
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) fb[t] = *(const i32x8*)(pb + t * 2048);
+  i32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+  for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int tm = 4 * (q & 1) + h, tn = q >> 1;
+        acc[tm][tn] = smfmac16<OP>(acc[tm][tn], fa[tm], fb[tn], idx[tm]);
+      }
+  }
+  uint32_t x = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x ^= (uint32_t)(acc[i][j][0] ^ acc[i][j][1] ^ acc[i][j][2] ^ acc[i][j][3]);
+  for (int off = 32; off > 0; off >>= 1) x ^= (uint32_t)__shfl_xor((int)x, off, 64);
+  if (l == 0) atomicXor(sink + blockIdx.x, x);
+}
+
 }  // namespace sp24
+
+extern "C" int sp24_calib_mfma(const void* a_vals, uint64_t a_bytes, const uint32_t* codes, uint64_t code_bytes,
+                               const void* b, uint64_t b_bytes, int a_type, int b_type, int rounds, int workgroups,
+                               uint32_t* sink, void* stream) {
+  const int op = sp24::op_for(a_type, b_type);
+  if (op < 0) return SP24_ERR_UNSUPPORTED;
+  if (!a_vals || !codes || !b || !sink || rounds < 1 || workgroups < 1) return SP24_ERR_INVALID_VALUE;
+  const uint64_t na = a_bytes / sp24::kCalibAUnit, nc = code_bytes / sp24::kCalibCUnit,
+                 nb = b_bytes / sp24::kCalibBUnit;
+  if (na == 0 || nc == 0 || nb == 0) return SP24_ERR_INVALID_VALUE;
+  if (((uintptr_t)a_vals | (uintptr_t)codes | (uintptr_t)b) & 15u) return SP24_ERR_MISALIGNED;
+  const char* pa = static_cast<const char*>(a_vals);
+  const char* pc = reinterpret_cast<const char*>(codes);
+  const char* pb = static_cast<const char*>(b);
+  const dim3 grid((unsigned)workgroups), block(sp24::kCalibWaves * 64);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (op) {
+#define SP24_CALIB_CASE(O)                                                                                    \
+  case sp24::O:                                                                                               \
+    hipLaunchKernelGGL(sp24::calib_mfma_kernel<sp24::O>, grid, block, 0, st, pa, na, pc, nc, pb, nb, rounds, sink); \
+    break;
+    SP24_CALIB_CASE(OP_F16)
+    SP24_CALIB_CASE(OP_BF16)
+    SP24_CALIB_CASE(OP_I8)
+    SP24_CALIB_CASE(OP_FP8_FP8)
+    SP24_CALIB_CASE(OP_FP8_BF8)
+    SP24_CALIB_CASE(OP_BF8_FP8)
+    SP24_CALIB_CASE(OP_BF8_BF8)
+#undef SP24_CALIB_CASE
+    default: return SP24_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? SP24_OK : SP24_ERR_LAUNCH;
+}
 
 extern "C" int sp24_calib_stream(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes,
                                  uint32_t* sink, int workgroups, int threads, void* stream) {

@@ -29,6 +29,18 @@ __host__ __device__ constexpr bool op_is_int(int op) { return op == OP_I8; }
 __host__ __device__ constexpr int op_kstep(int op) { return op_is_8bit(op) ? 128 : 64; }
 __host__ __device__ constexpr int op_esize(int op) { return op_is_8bit(op) ? 1 : 2; }
 
+// Sparse-MFMA operation for an (A, B) element-type pair, or -1.
+inline int op_for(int a, int b) {
+  if (a == SP24_F16 && b == SP24_F16) return OP_F16;
+  if (a == SP24_BF16 && b == SP24_BF16) return OP_BF16;
+  if (a == SP24_I8 && b == SP24_I8) return OP_I8;
+  if (a == SP24_FP8_E4M3 && b == SP24_FP8_E4M3) return OP_FP8_FP8;
+  if (a == SP24_FP8_E4M3 && b == SP24_BF8_E5M2) return OP_FP8_BF8;
+  if (a == SP24_BF8_E5M2 && b == SP24_FP8_E4M3) return OP_BF8_FP8;
+  if (a == SP24_BF8_E5M2 && b == SP24_BF8_E5M2) return OP_BF8_BF8;
+  return -1;
+}
+
 // One 16x16 sparse MFMA step.  Per lane: `a` = 16 bytes of compressed A
 // (8 values for 16-bit types, 16 for 8-bit), `b` = 32 bytes of dense B,
 // `idx` = this lane's 2-bit position codes (bits 2e.. for its element e; for

@@ -31,7 +31,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) >= 8 and "sp24_calib_stream" in names, names
+    assert len(names) >= 9 and {"sp24_calib_stream", "sp24_calib_mfma"} <= set(names), names
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
@@ -46,6 +46,22 @@ def test_calib_stream_argument_errors(L):
     assert f(P, 64, P, 32, P, 4, 96, None) == 1            # threads not a multiple of 64
     assert f(P + 8, 64, P, 32, P, 4, 256, None) == 3       # misaligned
     assert f(P, 0, 0, 0, P, 4, 256, None) == 0             # nothing to do, nothing launched
+
+
+def test_calib_mfma_argument_errors(L):
+    f = L.sp24_calib_mfma
+    F16, I8, BF = L.SP24_F16, L.SP24_I8, L.SP24_BF16
+    A, Mt, B, S = P, 2 * P, 3 * P, 4 * P
+    assert f(A, 8192, Mt, 2048, B, 8192, F16, BF, 1, 1, S, None) == 2          # mixed 16-bit pair
+    assert f(A, 8192, Mt, 2048, B, 8192, F16, 99, 1, 1, S, None) == 2          # unknown type
+    assert f(0, 8192, Mt, 2048, B, 8192, F16, F16, 1, 1, S, None) == 1         # null A
+    assert f(A, 8192, Mt, 2048, B, 8192, I8, I8, 1, 1, 0, None) == 1           # null sink
+    assert f(A, 8191, Mt, 2048, B, 8192, F16, F16, 1, 1, S, None) == 1         # fewer than 8 KiB of A
+    assert f(A, 8192, Mt, 2047, B, 8192, F16, F16, 1, 1, S, None) == 1         # fewer than 2 KiB of codes
+    assert f(A, 8192, Mt, 2048, B, 8191, F16, F16, 1, 1, S, None) == 1         # fewer than 8 KiB of B
+    assert f(A, 8192, Mt, 2048, B, 8192, F16, F16, 0, 1, S, None) == 1         # rounds < 1
+    assert f(A, 8192, Mt, 2048, B, 8192, F16, F16, 1, 0, S, None) == 1         # workgroups < 1
+    assert f(A + 8, 8192, Mt, 2048, B, 8192, F16, F16, 1, 1, S, None) == 3     # misaligned
 
 
 def test_size_queries(L):
