@@ -274,6 +274,44 @@ def mfma_ceiling(pkg, w, vals, meta, B, layout, stream, launches=10):
     return us, flop / us / 1e6, rounds, wgs
 
 
+def dense_reference(w, A, B, b_layout_nk, stream, launches=10):
+    """The same product with the dense, pruned A through the platform's own
+    dense GEMM (torch -> hipBLASLt): fp16 / bf16 with a 16-bit output
+    (torch.matmul), int8 with an int32 output (torch._int_mm), 8-bit floats
+    with an fp32 output (torch._scaled_mm, unit scales).  Returns (us, what)
+    or (None, reason).  Context for what the 2:4 layout buys; not part of
+    the step."""
+    import torch
+    from structured_sparse_matrix_sp24_amd import workloads as wl
+    Bkn = B.t() if b_layout_nk else B  # K x N view
+    try:
+        if w.a_type in (wl.F16, wl.BF16):
+            Bc = Bkn.contiguous()
+            fn = lambda: torch.matmul(A, Bc)  # noqa: E731
+            what = "torch.matmul (hipBLASLt), 16-bit output"
+        elif w.a_type == wl.I8:
+            Bc = Bkn.contiguous()
+            fn = lambda: torch._int_mm(A, Bc)  # noqa: E731
+            what = "torch._int_mm (hipBLASLt), int32 output"
+        else:
+            Bt = Bkn.t().contiguous().t()  # column-major K x N, as _scaled_mm wants
+            one = torch.ones((), dtype=torch.float32, device=A.device)
+            fn = lambda: torch._scaled_mm(A, Bt, one, one, out_dtype=torch.float32)  # noqa: E731
+            what = "torch._scaled_mm (hipBLASLt), fp32 output, unit scales"
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / launches * 1e3, what
+    except Exception as e:  # a type pair the platform library does not take
+        return None, f"not measured: {type(e).__name__}: {str(e)[:120]}"
+
+
 def measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream, ws, launches=20):
     """The calls adjacent to the hot path, each timed over back-to-back
     launches between two HIP events on the launch stream: sp24_decompress
@@ -343,6 +381,8 @@ def main():
                     help="skip the cold-cache measurement (compress and gemm rotating over 2 GiB of input copies)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the matrix-core ceiling (sp24_calib_mfma) of the large-N products")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip timing the same product through the platform's dense GEMM (context)")
     ap.add_argument("--next-rows", action="store_true",
                     help="also time the adjacent calls (decompress, validate_meta, 16-bit output with bias) "
                          "after the timed steps and add them to the line as next_rows")
@@ -459,6 +499,15 @@ def main():
     next_rows = measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream, ws) if args.next_rows else None
     cold = None if args.no_cold else measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream, ws)
     ceiling = None if (args.no_ceiling or w.N <= 64) else mfma_ceiling(pkg, w, vals, meta, B, layout, stream)
+    dense = None
+    if not args.no_dense:
+        # the pruned A, dense: the product the sparse kernel computes
+        Ap = torch.empty_like(A)
+        st = pkg.sp24_decompress(vals.data_ptr(), meta.data_ptr(), Ap.data_ptr(), w.M, w.K, w.a_type, layout, sh)
+        if st:
+            raise pkg.Sp24Error(st, "sp24_decompress")
+        dense = dense_reference(w, Ap, B, b_layout == pkg.SP24_B_NK, stream)
+        del Ap
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     flop = 2.0 * w.M * w.N * w.K
@@ -558,6 +607,12 @@ def main():
             "gemm_frac_of_ceiling": round(gemm_tflops / c_tf, 4),
             "launch": {"workgroups": c_wgs, "rounds": c_rounds},
         }
+    if dense is not None:
+        d_us, d_what = dense
+        res["dense_reference"] = {"what": d_what, "note": "the same product with the dense (pruned) A, for context"}
+        if d_us is not None:
+            res["dense_reference"].update({"us": round(d_us, 1), "TFLOP/s": round(flop / d_us / 1e6, 1),
+                                           "sparse_speedup": round(d_us / (gemm_ms * 1e3), 3)})
     if next_rows is not None:
         res["next_rows"] = next_rows
     if not args.no_cpu:
