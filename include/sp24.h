@@ -61,8 +61,9 @@
  *     every buffer.  The library keeps no state between calls and allocates
  *     no memory.
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
- *     Calls only enqueue work on it; they never synchronise.  A kernel fault
- *     shows up at the caller's next synchronisation.
+ *     Calls only enqueue kernels on it (no memset, no copy, no host
+ *     synchronisation), so they may be captured into a HIP graph.  A kernel
+ *     fault shows up at the caller's next synchronisation.
  *   - Argument errors are detected on the host, before anything is
  *     launched, and returned as an sp24_status code; nothing is enqueued.
  *   - Calls are thread-safe.
