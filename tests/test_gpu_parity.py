@@ -212,6 +212,34 @@ def test_gemm_random(pkg, a_type, b_type, M, N, K, layout):
     check_gemm_full(pkg, vals, meta, a_type, c.B, b_type, layout=layout)
 
 
+# More 256 x 256 tiles than compute units (several tiles per compute unit, the
+# dispatch order of the XCD-aware tile walk over a grid that is not a multiple
+# of 8), ragged M and N (edge tiles write fewer rows and columns), K of
+# exactly 3 k-steps, K ending in a partial k-step, both layouts and B layouts,
+# and beta != 0 (C read in the epilogue).  Every output is compared with the
+# oracle.
+@pytest.mark.slow
+@pytest.mark.parametrize("a_type,b_type", PAIRS)
+@pytest.mark.parametrize("M,N,K,layout,b_layout,beta", [
+    (4100, 4368, 192, KBLOCK, KN, 0.0),    # 16-bit: 3 k-steps
+    (4100, 4368, 384, KBLOCK, KN, 1.0),    # 8-bit: 3 k-steps
+    (4352, 4104, 544, ROW, NK, 0.0),       # partial last k-step
+    (4224, 4360, 416, KBLOCK, NK, 1.0),
+])
+def test_gemm_many_tiles(pkg, a_type, b_type, M, N, K, layout, b_layout, beta):
+    _say(f"gemm many tiles a={a_type} b={b_type} M={M} N={N} K={K} layout={layout} b_layout={b_layout} beta={beta}")
+    w = wl.random_case(41, M, N, K, a_type, b_type, beta=beta)
+    vals, meta = oracle.prune_compress(w.A, a_type)
+    D = run_gemm(pkg, vals, meta, a_type, w.B, b_type, w.C, w.alpha, w.beta, layout, b_layout).cpu().numpy()
+    ref, S = oracle_full_threaded(vals, meta, w)
+    if a_type == wl.I8:
+        assert np.array_equal(D.astype(np.int64), ref)
+    else:
+        err = np.abs(D.astype(np.float64) - ref)
+        bad = err > 1e-4 * S + 1e-6
+        assert not bad.any(), f"{bad.sum()} elements outside bound; worst ratio {np.max(err / (S + 1e-30)):.3g}"
+
+
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("a_type,b_type", PAIRS)
 @pytest.mark.parametrize("M,N,K", [(300, 272, 160), (512, 512, 544), (17, 96, 256), (96, 48, 352),
