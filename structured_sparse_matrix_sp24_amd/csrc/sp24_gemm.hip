@@ -547,14 +547,61 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   SP24_LDS float* scr = (SP24_LDS float*)((SP24_LDS char*)lS0 + w * (16 * kScrRow * 4));
   const int row_base = m0 + (w >> 2) * 128;
   const int col = n0 + (w & 3) * 64 + (l & 15) * 4;
+  // The slice's accumulators, row-major through the scratch: piece q of this
+  // lane is row (l/16) + 4q of slice tm, columns col .. col+3.
+  auto slice = [&](int tm, f32x4 v[4]) {
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      // cast the whole vector: a bit cast of one vector element is not safe here
+      const f32x4 a = __builtin_bit_cast(f32x4, acc[tm][tn]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) scr[(4 * (l >> 4) + r) * kScrRow + tn * 16 + (l & 15)] = a[r];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = *(const SP24_LDS f32x4*)(scr + ((l >> 4) + 4 * q) * kScrRow + (l & 15) * 4);
+  };
+  if (ep.beta != 0.0f && ep.out == OUT_32) {
+    // 32-bit output read back as C: the reads of C run kCPre slices ahead of
+    // the stores.  Read right before its store, each piece of C cost its wave
+    // a full memory round trip (32 per wave and tile, one after the other);
+    // here a slice's reads were issued kCPre slices earlier.  The reads come
+    // from clamped addresses inside C, so they need no bounds branch (a piece
+    // outside M x N is read from an element inside and never stored).  Rows
+    // of later slices are other elements than the ones stored before them,
+    // so reading them ahead of those stores is safe when C is also the
+    // output.
+    constexpr int kCPre = 4;
+    const int ccol = min(col, N - 4);
+    auto cload = [&](int tm, int q) -> i32x4 {
+      const int row = min(row_base + tm * 16 + (l >> 4) + 4 * q, M - 1);
+      return __builtin_nontemporal_load((const i32x4*)((const int*)C + (int64_t)row * N + ccol));
+    };
+    i32x4 cb[kCPre][4];
+#pragma unroll
+    for (int tm = 0; tm < kCPre; ++tm)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cb[tm][q] = cload(tm, q);
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm) {
+      f32x4 v[4];
+      slice(tm, v);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = row_base + tm * 16 + (l >> 4) + 4 * q;
+        const i32x4 c = cb[tm % kCPre][q];
+        if (tm + kCPre < 8) cb[tm % kCPre][q] = cload(tm + kCPre, q);
+        if (row < M && col < N) store_out4_c<op_is_int(OP)>(C, (int64_t)row * N + col, col, v[q], c, ep);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int tm = 0; tm < 8; ++tm) {
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn) {
-      // cast the whole vector: a bit cast of one vector element is not safe here
-      const f32x4 v = __builtin_bit_cast(f32x4, acc[tm][tn]);
+      const f32x4 a = __builtin_bit_cast(f32x4, acc[tm][tn]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) scr[(4 * (l >> 4) + r) * kScrRow + tn * 16 + (l & 15)] = v[r];
+      for (int r = 0; r < 4; ++r) scr[(4 * (l >> 4) + r) * kScrRow + tn * 16 + (l & 15)] = a[r];
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

@@ -148,6 +148,20 @@ __device__ __forceinline__ void store_out4(void* C, int64_t o, int col, f32x4 v,
   }
 }
 
+// store_out4 for a 32-bit output with beta != 0, with the four C values
+// (their bits) already read: the same arithmetic.
+template <bool INT>
+__device__ __forceinline__ void store_out4_c(void* C, int64_t o, int col, f32x4 v, i32x4 c, const Epilogue& ep) {
+  if constexpr (INT) {
+    __builtin_nontemporal_store(__builtin_bit_cast(i32x4, v) + c, (i32x4*)((int*)C + o));
+  } else {
+    f32x4 d = v * ep.alpha;
+    d += ep.beta * __builtin_bit_cast(f32x4, c);
+    if (ep.bias) d += *(const f32x4*)(ep.bias + col);
+    __builtin_nontemporal_store(d, (f32x4*)((float*)C + o));
+  }
+}
+
 // One output element (same arithmetic as store_out4).
 template <bool INT>
 __device__ __forceinline__ void store_out1(void* C, int64_t o, int col, float v, const Epilogue& ep) {
