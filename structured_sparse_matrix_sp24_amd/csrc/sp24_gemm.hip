@@ -560,21 +560,20 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = *(const SP24_LDS f32x4*)(scr + ((l >> 4) + 4 * q) * kScrRow + (l & 15) * 4);
   };
+  // beta != 0: the reads of C run kCPre slices ahead of the stores.  Read
+  // right before its store, each piece of C cost its wave a full memory
+  // round trip (32 per wave and tile, one after the other); here a slice's
+  // reads were issued kCPre slices earlier.  The reads come from clamped
+  // addresses inside C, so they need no bounds branch (a piece outside M x N
+  // is read from an element inside and never stored).  Rows of later slices
+  // are other elements than the ones stored before them, so reading them
+  // ahead of those stores is safe when C is also the output.
+  constexpr int kCPre = 4;
+  const int ccol = min(col, N - 4);
+  auto crow = [&](int tm, int q) { return (int64_t)min(row_base + tm * 16 + (l >> 4) + 4 * q, M - 1); };
   if (ep.beta != 0.0f && ep.out == OUT_32) {
-    // 32-bit output read back as C: the reads of C run kCPre slices ahead of
-    // the stores.  Read right before its store, each piece of C cost its wave
-    // a full memory round trip (32 per wave and tile, one after the other);
-    // here a slice's reads were issued kCPre slices earlier.  The reads come
-    // from clamped addresses inside C, so they need no bounds branch (a piece
-    // outside M x N is read from an element inside and never stored).  Rows
-    // of later slices are other elements than the ones stored before them,
-    // so reading them ahead of those stores is safe when C is also the
-    // output.
-    constexpr int kCPre = 4;
-    const int ccol = min(col, N - 4);
     auto cload = [&](int tm, int q) -> i32x4 {
-      const int row = min(row_base + tm * 16 + (l >> 4) + 4 * q, M - 1);
-      return __builtin_nontemporal_load((const i32x4*)((const int*)C + (int64_t)row * N + ccol));
+      return __builtin_nontemporal_load((const i32x4*)((const int*)C + crow(tm, q) * N + ccol));
     };
     i32x4 cb[kCPre][4];
 #pragma unroll
@@ -594,6 +593,35 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
       }
     }
     return;
+  }
+  if constexpr (!op_is_int(OP)) {
+    if (ep.beta != 0.0f) {  // 16-bit output and C
+      auto cload = [&](int tm, int q) -> i32x2 {
+        return __builtin_nontemporal_load((const i32x2*)((const short*)C + crow(tm, q) * N + ccol));
+      };
+      const bool bf = ep.out == OUT_BF16;
+      i32x2 cb[kCPre][4];
+#pragma unroll
+      for (int tm = 0; tm < kCPre; ++tm)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cb[tm][q] = cload(tm, q);
+#pragma unroll
+      for (int tm = 0; tm < 8; ++tm) {
+        f32x4 v[4];
+        slice(tm, v);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = row_base + tm * 16 + (l >> 4) + 4 * q;
+          const i32x2 c = cb[tm % kCPre][q];
+          if (tm + kCPre < 8) cb[tm % kCPre][q] = cload(tm + kCPre, q);
+          if (row < M && col < N) {
+            if (bf) store_out4_c16<true>(C, (int64_t)row * N + col, col, v[q], c, ep);
+            else store_out4_c16<false>(C, (int64_t)row * N + col, col, v[q], c, ep);
+          }
+        }
+      }
+      return;
+    }
   }
 #pragma unroll
   for (int tm = 0; tm < 8; ++tm) {

@@ -162,6 +162,22 @@ __device__ __forceinline__ void store_out4_c(void* C, int64_t o, int col, f32x4 
   }
 }
 
+// store_out4 for a 16-bit output (BF: bfloat16, else fp16) with beta != 0,
+// with the four C values (their bits) already read: the same arithmetic.
+template <bool BF>
+__device__ __forceinline__ void store_out4_c16(void* C, int64_t o, int col, f32x4 v, i32x2 c, const Epilogue& ep) {
+  f32x4 d = v * ep.alpha;
+  if constexpr (BF) {
+    d += ep.beta * __builtin_convertvector(__builtin_bit_cast(bf16x4, c), f32x4);
+    if (ep.bias) d += *(const f32x4*)(ep.bias + col);
+    __builtin_nontemporal_store(__builtin_convertvector(d, bf16x4), (bf16x4*)((__bf16*)C + o));
+  } else {
+    d += ep.beta * __builtin_convertvector(__builtin_bit_cast(f16x4, c), f32x4);
+    if (ep.bias) d += *(const f32x4*)(ep.bias + col);
+    __builtin_nontemporal_store(__builtin_convertvector(d, f16x4), (f16x4*)((_Float16*)C + o));
+  }
+}
+
 // One output element (same arithmetic as store_out4).
 template <bool INT>
 __device__ __forceinline__ void store_out1(void* C, int64_t o, int col, float v, const Epilogue& ep) {
