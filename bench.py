@@ -33,6 +33,22 @@ sys.path.insert(0, ROOT)
 # SIMD: 1024 SIMDs * 2048 flop/clk * 2.4 GHz = 5033 TFLOP/s).
 PEAK_SPARSE_TFLOPS = {"fp16": 5033.2, "bf16": 5033.2, "int8": 10066.3, "fp8": 10066.3}
 PEAK_HBM_GBPS = 8000.0
+
+# Call bookkeeping for kernel-trace summaries.  Each library call here
+# launches exactly one kernel, so counting the calls of each entry point
+# tells which dispatches of a trace of this run belong to which measured
+# region; the regions are printed to stderr at the end ("bench-regions").
+CALLS = {"compress": 0, "gemm": 0, "stream": 0}
+REGIONS = {}
+
+
+def region_open(name, key):
+    REGIONS[name] = {"calls_of": key, "first": CALLS[key]}
+
+
+def region_close(name):
+    r = REGIONS[name]
+    r["end"] = CALLS[r["calls_of"]]
 # the headline metric (the default workload); other workloads name themselves
 METRIC = "dense-equiv TFLOP/s of 2:4 sparse GEMM (fp16, 8192^3) + % of smfmac peak"
 
@@ -164,6 +180,7 @@ def stream_floor(pkg, read_bytes, write_bytes, workgroups, threads, stream, rot_
     def one(i):
         st = pkg.sp24_calib_stream(src[i].data_ptr(), read_bytes, dst[i].data_ptr(), write_bytes, sink.data_ptr(),
                                    workgroups, threads, sh)
+        CALLS["stream"] += 1
         if st:
             raise pkg.Sp24Error(st, "sp24_calib_stream")
 
@@ -171,10 +188,13 @@ def stream_floor(pkg, read_bytes, write_bytes, workgroups, threads, stream, rot_
         one(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    name = f"stream_floor_{read_bytes}_{write_bytes}_{workgroups}_{threads}"
+    region_open(name, "stream")
     e0.record(stream)
     for i in range(n):
         one(i)
     e1.record(stream)
+    region_close(name)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / n * 1e3
     del src, dst
@@ -195,17 +215,19 @@ def measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream, ws, rot_
     import torch
     sh = stream.cuda_stream
 
-    def rotate(tensors, bytes_each, fn):
+    def rotate(tensors, bytes_each, fn, key):
         n = max(2, -(-rot_bytes // max(1, bytes_each)))
         copies = [[t.clone() for t in tensors] for _ in range(n)]
         torch.cuda.synchronize()
         for c in copies:
             fn(*c)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        region_open("cold_" + key, key)
         e0.record(stream)
         for c in copies:
             fn(*c)
         e1.record(stream)
+        region_close("cold_" + key)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / n * 1e3
         del copies
@@ -217,15 +239,17 @@ def measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream, ws, rot_
             raise pkg.Sp24Error(st, what)
 
     def comp(a, v, m):
+        CALLS["compress"] += 1
         check(pkg.sp24_prune_compress(a.data_ptr(), v.data_ptr(), m.data_ptr(), w.M, w.K, w.a_type, layout, sh),
               "sp24_prune_compress")
 
     cb = vals.numel() * vals.element_size() + meta.numel() * meta.element_size()
     ab = A.numel() * A.element_size()
-    comp_us, nc = rotate([A, vals, meta], ab + cb, comp)
+    comp_us, nc = rotate([A, vals, meta], ab + cb, comp, "compress")
     big_b = B.numel() * B.element_size() > (1 << 20)
 
     def gem(v, m, *rest):
+        CALLS["gemm"] += 1
         b = rest[0] if big_b else B
         check(pkg.sp24_gemm(v.data_ptr(), m.data_ptr(), w.a_type, layout, b.data_ptr(), w.b_type, b_layout,
                             C.data_ptr(), w.M, w.N, w.K, w.alpha, w.beta, ws.data_ptr(), ws.numel(), sh),
@@ -233,16 +257,20 @@ def measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream, ws, rot_
 
     gin = [vals, meta] + ([B] if big_b else [])
     gbytes = sum(t.numel() * t.element_size() for t in gin)
-    gemm_us, ng = rotate(gin, gbytes, gem)
+    gemm_us, ng = rotate(gin, gbytes, gem, "gemm")
     return comp_us, nc, gemm_us, ng
 
 
-def mfma_ceiling(pkg, w, vals, meta, B, layout, stream, launches=10):
-    """TFLOP/s (dense-equivalent) of sp24_calib_mfma: the product's sparse
+def mfma_ceiling(pkg, w, vals, meta, B, layout, stream, launches=10, shape=16, loads=False):
+    """TFLOP/s (dense-equivalent) of sp24_calib_mfma_ex: the product's sparse
     instructions for this type pair with their operands (taken from this
     workload's compressed A, codes and B) held in registers, no memory
     traffic.  One workgroup per CU and as many instructions per launch as the
-    product issues; back-to-back launches between two HIP events."""
+    product issues; back-to-back launches between two HIP events.  shape 32
+    issues the 32x32 instructions of the pair instead (the same work);
+    loads=True adds the product's direct-to-LDS loads per wave and k-step
+    (1 KiB each, from the first 2 MiB of B, which stays in the L2 as the
+    product's staged tiles mostly do)."""
     import torch
     from structured_sparse_matrix_sp24_amd import workloads as wl
     kstep = 64 if wl.ESIZE[w.a_type] == 2 else 128
@@ -253,12 +281,13 @@ def mfma_ceiling(pkg, w, vals, meta, B, layout, stream, launches=10):
     vb = pkg.sp24_values_bytes(w.M, w.K, w.a_type, layout)
     mb = pkg.sp24_meta_bytes(w.M, w.K, w.a_type, layout)
     bb = B.numel() * B.element_size()
+    src, src_bytes = (B.data_ptr(), min(bb, 2 << 20)) if loads else (None, 0)
 
     def one():
-        st = pkg.sp24_calib_mfma(vals.data_ptr(), vb, meta.data_ptr(), mb, B.data_ptr(), bb, w.a_type, w.b_type,
-                                 rounds, wgs, sink.data_ptr(), stream.cuda_stream)
+        st = pkg.sp24_calib_mfma_ex(vals.data_ptr(), vb, meta.data_ptr(), mb, B.data_ptr(), bb, w.a_type, w.b_type,
+                                    rounds, wgs, shape, src, src_bytes, sink.data_ptr(), stream.cuda_stream)
         if st:
-            raise pkg.Sp24Error(st, "sp24_calib_mfma")
+            raise pkg.Sp24Error(st, "sp24_calib_mfma_ex")
 
     for _ in range(3):
         one()
@@ -354,10 +383,13 @@ def measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream, ws, launc
     if w.a_type != wl.I8:
         D16 = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda:0")
         bias = torch.ones(w.N, dtype=torch.float32, device="cuda:0")
-        us = timed(lambda: check(pkg.sp24_gemm_ex(vals.data_ptr(), meta.data_ptr(), w.a_type, layout, B.data_ptr(),
-                                                  w.b_type, b_layout, D16.data_ptr(), wl.F16, bias.data_ptr(), w.M,
-                                                  w.N, w.K, 1.0, 0.0, ws.data_ptr(), ws.numel(), sh),
-                                 "sp24_gemm_ex"), 5)
+        def gemm_ex():
+            CALLS["gemm"] += 1  # the same product kernel as sp24_gemm
+            check(pkg.sp24_gemm_ex(vals.data_ptr(), meta.data_ptr(), w.a_type, layout, B.data_ptr(), w.b_type,
+                                   b_layout, D16.data_ptr(), wl.F16, bias.data_ptr(), w.M, w.N, w.K, 1.0, 0.0,
+                                   ws.data_ptr(), ws.numel(), sh), "sp24_gemm_ex")
+
+        us = timed(gemm_ex, 5)
         tf = 2.0 * w.M * w.N * w.K / (us * 1e-6) / 1e12
         out["gemm_ex_f16_out_bias"] = {"us": round(us, 1), "TFLOP/s": round(tf, 1)}
     return out
@@ -444,12 +476,14 @@ def main():
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     def compress():
+        CALLS["compress"] += 1
         st = pkg.sp24_prune_compress(A.data_ptr(), vals.data_ptr(), meta.data_ptr(), w.M, w.K, w.a_type, layout,
                                       sh)
         if st:
             raise pkg.Sp24Error(st, "sp24_prune_compress")
 
     def gemm():
+        CALLS["gemm"] += 1
         st = pkg.sp24_gemm(vals.data_ptr(), meta.data_ptr(), w.a_type, layout, B.data_ptr(), w.b_type, b_layout,
                            C.data_ptr(), w.M, w.N, w.K, w.alpha, w.beta, ws.data_ptr(), ws_bytes, sh)
         if st:
@@ -475,6 +509,8 @@ def main():
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    region_open("steps_compress", "compress")
+    region_open("steps_gemm", "gemm")
     t0 = time.perf_counter()
     for s in range(args.steps):
         e0, e1, e2 = ev[s]
@@ -485,6 +521,8 @@ def main():
         e2.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    region_close("steps_compress")
+    region_close("steps_gemm")
     if C0 is not None:
         # the timed loop accumulated beta*C repeatedly; restore and run one clean step
         reset_c()
@@ -498,7 +536,12 @@ def main():
     torch.cuda.synchronize()
     next_rows = measure_next_rows(pkg, w, vals, meta, B, layout, b_layout, stream, ws) if args.next_rows else None
     cold = None if args.no_cold else measure_cold(pkg, w, A, vals, meta, B, C, layout, b_layout, stream, ws)
-    ceiling = None if (args.no_ceiling or w.N <= 64) else mfma_ceiling(pkg, w, vals, meta, B, layout, stream)
+    ceiling = variants = None
+    if not (args.no_ceiling or w.N <= 64):
+        ceiling = mfma_ceiling(pkg, w, vals, meta, B, layout, stream)
+        variants = {name: mfma_ceiling(pkg, w, vals, meta, B, layout, stream, shape=sh_, loads=ld_)
+                    for name, sh_, ld_ in (("with_loads", 16, True), ("shape_32x32", 32, False),
+                                           ("shape_32x32_with_loads", 32, True))}
     dense = None
     if not args.no_dense:
         # the pruned A, dense: the product the sparse kernel computes
@@ -606,7 +649,14 @@ def main():
             "frac_sparse_peak": round(c_tf / PEAK_SPARSE_TFLOPS[label], 4),
             "gemm_frac_of_ceiling": round(gemm_tflops / c_tf, 4),
             "launch": {"workgroups": c_wgs, "rounds": c_rounds},
+            "variants_note": "with_loads: the same stream with the product's direct-to-LDS loads per wave and k-step "
+                             "issued between the instructions (no fragment reads); shape_32x32: the pair's 32x32 "
+                             "sparse instructions instead, the same work",
         }
+        for name, (v_us, v_tf, _, _) in variants.items():
+            res["mfma_ceiling"][name] = {"us": round(v_us, 1), "TFLOP/s": round(v_tf, 1),
+                                         "frac_sparse_peak": round(v_tf / PEAK_SPARSE_TFLOPS[label], 4),
+                                         "gemm_frac": round(gemm_tflops / v_tf, 4)}
     if dense is not None:
         d_us, d_what = dense
         res["dense_reference"] = {"what": d_what, "note": "the same product with the dense (pruned) A, for context"}
@@ -622,6 +672,7 @@ def main():
             # host (measured): ~4.8e11 of them is ~15 s on 16 cores (capped at all M rows)
             rows = max(1, min(w.M, int(4.8e11 / max(1, w.N * w.K // 2))))
         res["cpu_baseline"] = cpu_baseline(w, rows)
+    print("bench-regions " + json.dumps(REGIONS), file=sys.stderr, flush=True)
     print(json.dumps(res), flush=True)
 
 

@@ -7,7 +7,9 @@
  *   - the product's sparse matrix-core instruction stream with its operands
  *     held in registers, to measure the rate the matrix cores sustain on the
  *     workload's own operand values (their power draw depends on the data,
- *     and the clock on the power).
+ *     and the clock on the power); optionally with the product's
+ *     direct-to-LDS loads issued between the instructions, or with the
+ *     32x32 instruction shape in place of 16x16.
  * The benchmark reports each kernel against both the measured figure and
  * the published peak.
  */
@@ -73,6 +75,35 @@ int sp24_calib_stream(const void* src, uint64_t read_bytes, void* dst, uint64_t 
  */
 int sp24_calib_mfma(const void* a_vals, uint64_t a_bytes, const uint32_t* codes, uint64_t code_bytes, const void* b,
                     uint64_t b_bytes, int a_type, int b_type, int rounds, int workgroups, uint32_t* sink, void* stream);
+
+/*
+ * sp24_calib_mfma_ex -- sp24_calib_mfma with two variations of the
+ * instruction stream (sp24_calib_mfma is this call with shape 16 and no
+ * load source):
+ *   shape 16   the product's 16x16 instructions (32 per round);
+ *   shape 32   the 32x32 sparse instructions of the same pair (32x32x32 for
+ *              16-bit types, 32x32x64 for 8-bit), 16 per round over the
+ *              same operand registers read as 32x32 fragments; the same
+ *              work per round, so the dense-equivalent work per launch is
+ *              the formula above for either shape;
+ *   load_src   NULL, or a DEVICE buffer (16-byte aligned, at least 1024
+ *              bytes): then every wave also issues, per round, the
+ *              product's number of 1 KiB direct-to-LDS loads per wave and
+ *              k-step (7 for 16-bit types, 8 for 8-bit), one after each
+ *              of the first 7 or 8 of the round's 8 instruction groups, in
+ *              the product's form (an LDS base and a per-lane offset set
+ *              for each load), reading consecutive 1 KiB blocks of the
+ *              largest power-of-two prefix of load_src (at most 1 GiB) into
+ *              a 16 KiB LDS ring per wave; each round waits for the loads of
+ *              the round before.  The loads change no result: the sinks
+ *              equal those of the same call without them.
+ * Errors: as sp24_calib_mfma, and SP24_ERR_INVALID_VALUE for a shape other
+ * than 16 or 32 or a load source under 1024 bytes.  Enqueues on `stream`
+ * only.
+ */
+int sp24_calib_mfma_ex(const void* a_vals, uint64_t a_bytes, const uint32_t* codes, uint64_t code_bytes,
+                       const void* b, uint64_t b_bytes, int a_type, int b_type, int rounds, int workgroups, int shape,
+                       const void* load_src, uint64_t load_src_bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -64,6 +64,8 @@ def lib():
         U64 = ctypes.c_uint64
         L.sp24_calib_mfma.argtypes = [P, U64, P, U64, P, U64, I, I, I, I, P, P]
         L.sp24_calib_mfma.restype = I
+        L.sp24_calib_mfma_ex.argtypes = [P, U64, P, U64, P, U64, I, I, I, I, I, P, U64, P, P]
+        L.sp24_calib_mfma_ex.restype = I
         _lib = L
     return _lib
 
@@ -126,6 +128,15 @@ def sp24_calib_mfma(a_vals: int, a_bytes: int, codes: int, code_bytes: int, b: i
     instruction stream with its operands in registers."""
     return lib().sp24_calib_mfma(a_vals, a_bytes, codes, code_bytes, b, b_bytes, a_type, b_type, rounds, workgroups,
                                  sink, stream)
+
+
+def sp24_calib_mfma_ex(a_vals: int, a_bytes: int, codes: int, code_bytes: int, b: int, b_bytes: int, a_type: int,
+                       b_type: int, rounds: int, workgroups: int, shape: int, load_src, load_src_bytes: int,
+                       sink: int, stream) -> int:
+    """Measurement aid (include/sp24_calib.h): sp24_calib_mfma with the
+    32x32 instruction shape and / or the product's direct-to-LDS loads."""
+    return lib().sp24_calib_mfma_ex(a_vals, a_bytes, codes, code_bytes, b, b_bytes, a_type, b_type, rounds,
+                                    workgroups, shape, load_src, load_src_bytes, sink, stream)
 
 
 def sp24_version() -> int:

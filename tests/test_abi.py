@@ -64,6 +64,18 @@ def test_calib_mfma_argument_errors(L):
     assert f(A + 8, 8192, Mt, 2048, B, 8192, F16, F16, 1, 1, S, None) == 3     # misaligned
 
 
+def test_calib_mfma_ex_argument_errors(L):
+    f = L.sp24_calib_mfma_ex
+    F16, I8 = L.SP24_F16, L.SP24_I8
+    A, Mt, B, S, Src = P, 2 * P, 3 * P, 4 * P, 5 * P
+    assert f(A, 8192, Mt, 2048, B, 8192, F16, F16, 1, 1, 8, None, 0, S, None) == 1      # shape 8
+    assert f(A, 8192, Mt, 2048, B, 8192, F16, F16, 1, 1, 64, None, 0, S, None) == 1     # shape 64
+    assert f(A, 8192, Mt, 2048, B, 8192, I8, I8, 1, 1, 32, Src, 1023, S, None) == 1     # load source < 1 KiB
+    assert f(A, 8192, Mt, 2048, B, 8192, I8, I8, 1, 1, 32, Src + 4, 4096, S, None) == 3  # misaligned source
+    assert f(A, 8192, Mt, 2048, B, 8192, F16, L.SP24_BF16, 1, 1, 32, None, 0, S, None) == 2  # mixed pair
+    assert f(0, 8192, Mt, 2048, B, 8192, F16, F16, 1, 1, 16, Src, 4096, S, None) == 1   # null A
+
+
 def test_size_queries(L):
     ROW, KB = L.SP24_LAYOUT_ROW, L.SP24_LAYOUT_KBLOCK
     assert L.sp24_values_bytes(8192, 8192, L.SP24_F16, ROW) == 8192 * 4096 * 2
