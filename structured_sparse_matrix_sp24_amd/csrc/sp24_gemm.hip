@@ -79,6 +79,7 @@ __host__ __device__ constexpr int meta_step_bytes() { return op_esize(OP) == 2 ?
 // publishes that step before group 0 reads it in phase 2k+1.
 // ----------------------------------------------------------------------------
 constexpr int kBM = 256, kBN = 256, kThreads8 = 512;
+constexpr int64_t kComputeUnits = 256;  // MI355X
 constexpr int kLdsA = kBM * 64;                   // 16 KiB
 constexpr int kLdsB = 32768;                      // KS * BN * esize = 32 KiB for both families
 constexpr int kLdsM = kBM * 16;                   // 4 KiB (16-bit inputs use half)
@@ -222,6 +223,12 @@ struct TileArgs {
   int64_t ldbk;    // N x K: bytes per row of B
   int M, N, m0, n0, nsteps, nfull;
   int Mp;          // KBLOCK: metadata rows per block (M rounded up to 128)
+  // beta != 0: the tile's C read ahead into the caches during the last
+  // k-steps (see gemm_large8_kernel)
+  i32x4 rC;        // C from the tile's first element on
+  uint32_t pf_row_bytes;  // bytes of C per piece of rows (N * csize * rows per piece)
+  int pf_j0;       // first load step of the window
+  int pf_pieces;   // pieces of the tile
 };
 
 // Everything this wave's loads of k-step j need, computed ahead of the phase
@@ -241,6 +248,7 @@ struct DmaStep {
   uint32_t vA[2];   // A: per-lane offsets of the two pieces
   uint32_t vM[2];   // metadata: per-lane offsets
   uint32_t vB[4];   // B: per-lane offsets
+  uint32_t sPF;     // C read-ahead: the piece's byte offset (a scalar), or 2^31 outside the window
 };
 
 template <bool B>
@@ -248,12 +256,21 @@ struct BoolC {
   static constexpr bool value = B;
 };
 
-template <int OP, int LAYOUT, int BL, bool MASK>
+template <int OP, int LAYOUT, int BL, bool MASK, bool PF = false>
 __device__ __forceinline__ DmaStep make_dma_step(SP24_LDS char* st, const TileArgs& ta, const LaneConsts8& lc,
-                                                 int j) {
+                                                 int j, int w) {
   constexpr int KS = op_kstep(OP), ES = op_esize(OP), MB = meta_step_bytes<OP>();
   DmaStep d;
   d.lds = lds_addr(st);
+  if constexpr (PF) {
+    // piece p of the tile's C for wave w in load step j (uniform)
+    // (outside the window the offset 2^31 puts every lane past the range,
+    // which is below 2^31, without wrapping: a lane's own offset is below
+    // 2^23 when 256 rows of C span less than 2 GiB)
+    const int p = (j - ta.pf_j0) * 8 + w;
+    const bool in = p >= 0 && p < ta.pf_pieces;
+    d.sPF = in ? (uint32_t)p * ta.pf_row_bytes : 0x80000000u;
+  }
   if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK) {
     const bool in = j < ta.nsteps;
     d.rA = make_rsrc4(ta.A_vals + ((int64_t)j * ta.M + ta.m0) * 64, in ? (uint64_t)(ta.M - ta.m0) * 64 : 0u);
@@ -334,7 +351,13 @@ __device__ __forceinline__ void phase_end() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int OP, int LAYOUT, int BL>
+// PF (launched when beta != 0): during the last k-steps every wave also reads
+// one 1 KiB piece of the tile's C per step (a tile row of a 32-bit C, two
+// rows of a 16-bit one) into a scratch kilobyte of LDS that nothing reads, so
+// that the epilogue finds C in the caches.  With every tile reaching its
+// epilogue at the same moment (one tile per CU at 4096^3), C otherwise comes
+// from HBM in one burst with the output.
+template <int OP, int LAYOUT, int BL, bool PF>
 __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __restrict__ A_vals,
                                                                  const char* __restrict__ meta,
                                                                  const char* __restrict__ B, void* C, int M, int N,
@@ -342,12 +365,14 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
                                                                  int tiles_n) {
   // One LDS object per stage.
   __shared__ __attribute__((aligned(1024))) char lS0[kLdsStage], lS1[kLdsStage], lS2[kLdsStage];
+  __shared__ __attribute__((aligned(1024))) char lPF[PF ? 1024 : 16];
   // (uniform selects; an array of LDS pointers would become a table in memory)
   auto st = [&](int i) -> SP24_LDS char* {
     return i == 0 ? (SP24_LDS char*)lS0 : (i == 1 ? (SP24_LDS char*)lS1 : (SP24_LDS char*)lS2);
   };
   constexpr int KS = op_kstep(OP), ES = op_esize(OP), MB = meta_step_bytes<OP>();
-  constexpr int L = loads_per_step<OP>();
+  constexpr int LD = loads_per_step<OP>();  // loads of operands per wave and k-step
+  constexpr int L = LD + (PF ? 1 : 0);       // all loads per wave and k-step
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous range of tiles so neighbouring tiles share its L2, then walk
@@ -390,6 +415,23 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   const LaneConsts8 lc =
       make_lane_consts8<OP, LAYOUT, BL>(w, l, ta.rowA, ta.rowM, BL == SP24_B_NK ? K * ES : N * ES);
   const int nsteps = ta.nsteps;
+  // C read-ahead: a piece is 1 KiB, one tile row of a 32-bit C or two of a
+  // 16-bit one (lanes 0-31 the first, 32-63 the second).  The launcher uses
+  // PF only when 256 rows of C span less than 2 GiB, so every offset fits in
+  // 32 bits; rows past M fall outside the range, and a lane past N reads
+  // other bytes of C, which only warms the caches.  The window is the last
+  // 32 load steps (loads are issued up to step nsteps + 2).
+  uint32_t voC = 0, pf_lds = 0;
+  if constexpr (PF) {
+    const int csize = ep.out == OUT_32 ? 4 : 2, lpr = csize == 4 ? 64 : 32;
+    ta.rC = make_rsrc4((const char*)C + ((int64_t)m0 * N + n0) * csize,
+                       (uint64_t)((int64_t)min(M - m0, kBM) * N - n0) * csize);
+    ta.pf_row_bytes = (uint32_t)(64 / lpr) * (uint32_t)N * (uint32_t)csize;
+    ta.pf_pieces = kBM / (64 / lpr);
+    ta.pf_j0 = max(0, nsteps + 3 - 32);
+    voC = (uint32_t)(l / lpr) * (uint32_t)N * (uint32_t)csize + 16u * (uint32_t)(l % lpr);
+    pf_lds = lds_addr((SP24_LDS char*)lPF);
+  }
 
   i32x4 acc[8][4];
 #pragma unroll
@@ -441,7 +483,7 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   };
   // All loads of this wave's share of step j, back to back (pipeline fill).
   auto dma_all = [&](int j) {
-    const DmaStep d = make_dma_step<OP, LAYOUT, BL, true>(st(j % 3), ta, lc, j);
+    const DmaStep d = make_dma_step<OP, LAYOUT, BL, true, PF>(st(j % 3), ta, lc, j, w);
     dma_piece<OP, LAYOUT, BL, 0>(d, w);
     dma_piece<OP, LAYOUT, BL, 1>(d, w);
     dma_piece<OP, LAYOUT, BL, 2>(d, w);
@@ -449,7 +491,8 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
     dma_piece<OP, LAYOUT, BL, 4>(d, w);
     dma_piece<OP, LAYOUT, BL, 5>(d, w);
     dma_piece<OP, LAYOUT, BL, 6>(d, w);
-    if constexpr (L == 8) dma_piece<OP, LAYOUT, BL, 7>(d, w);
+    if constexpr (LD == 8) dma_piece<OP, LAYOUT, BL, 7>(d, w);
+    if constexpr (PF) dma16_asm(ta.rC, pf_lds, voC, d.sPF);
   };
   // Staging phase: the fragments of step jr.
   auto stage_phase = [&](int jr) {
@@ -485,8 +528,10 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
       if (q == 4) dma_piece<OP, LAYOUT, BL, 4>(d, w);
       if (q == 5) dma_piece<OP, LAYOUT, BL, 5>(d, w);
       if (q == 6) dma_piece<OP, LAYOUT, BL, 6>(d, w);
-      if constexpr (L == 8)
+      if constexpr (LD == 8)
         if (q == 7) dma_piece<OP, LAYOUT, BL, 7>(d, w);
+      if constexpr (PF)
+        if (q == 7) dma16_asm(ta.rC, pf_lds, voC, d.sPF);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -506,12 +551,12 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   if (g0) {
     phase_end<L>();  // this wave's share of step 0 has landed
     stage_phase(0);
-    DmaStep d = make_dma_step<OP, LAYOUT, BL, true>(st(2), ta, lc, 2);
+    DmaStep d = make_dma_step<OP, LAYOUT, BL, true, PF>(st(2), ta, lc, 2, w);
     auto iter = [&](int k, auto mask) {
       mfma_phase(d);              // phase 2k: step k, loads of step k+2
       phase_end<L>();             // this wave's share of step k+1 has landed
       stage_phase(k + 1);         // phase 2k+1
-      d = make_dma_step<OP, LAYOUT, BL, decltype(mask)::value>(st((k + 3) % 3), ta, lc, k + 3);
+      d = make_dma_step<OP, LAYOUT, BL, decltype(mask)::value, PF>(st((k + 3) % 3), ta, lc, k + 3, w);
       phase_end<63>();            // the reads of step k+1 are done
     };
     int k = 0;
@@ -522,7 +567,7 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
     phase_end<2 * L>();
     auto iter = [&](int k, auto mask) {
       stage_phase(k);             // phase 2k
-      const DmaStep d = make_dma_step<OP, LAYOUT, BL, decltype(mask)::value>(st(k % 3), ta, lc, k + 3);
+      const DmaStep d = make_dma_step<OP, LAYOUT, BL, decltype(mask)::value, PF>(st(k % 3), ta, lc, k + 3, w);
       phase_end<L>();             // this wave's share of step k+1 has landed, the reads of step k are done
       mfma_phase(d);              // phase 2k+1: step k, loads of step k+3
       phase_end<63>();
@@ -947,8 +992,20 @@ static hipError_t launch_op(const void* A_vals, const uint32_t* meta, const void
     return hipGetLastError();
   }
   const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
-  hipLaunchKernelGGL((gemm_large8_kernel<OP, LAYOUT, BL>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads8), 0,
-                     stream, a, m, b, C, M, N, K, ep, tiles_m, tiles_n);
+  // C read ahead during the main loop only when every tile runs at once (at
+  // most one per compute unit), so that all epilogues would otherwise read C
+  // from HBM in the same burst: fp16 4096^3 with beta = 1 93.0 -> 87.1 us.
+  // With more tiles the epilogues are spread out and the C read of each is
+  // hidden by reading ahead in the epilogue itself, while the extra loads and
+  // the C lines in the caches cost the main loop (fp16 8192^3, beta = 1:
+  // 559 -> 569 us with it).
+  const int64_t csize = ep.out == OUT_32 ? 4 : 2;
+  if (ep.beta != 0.0f && (int64_t)tiles_m * tiles_n <= kComputeUnits && (int64_t)kBM * N * csize < (1ll << 31))
+    hipLaunchKernelGGL((gemm_large8_kernel<OP, LAYOUT, BL, true>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(kThreads8), 0, stream, a, m, b, C, M, N, K, ep, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_large8_kernel<OP, LAYOUT, BL, false>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(kThreads8), 0, stream, a, m, b, C, M, N, K, ep, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
