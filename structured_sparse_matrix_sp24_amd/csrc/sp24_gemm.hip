@@ -351,13 +351,15 @@ __device__ __forceinline__ void phase_end() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// PF (launched when beta != 0): during the last k-steps every wave also reads
+// MODE 0: streaming output stores (more tiles than compute units).  MODE 1
+// and 2 (every tile runs at once; K-blocked layout): ordinary output stores,
+// and in MODE 2 (beta != 0) also PF: during the last k-steps every wave also reads
 // one 1 KiB piece of the tile's C per step (a tile row of a 32-bit C, two
 // rows of a 16-bit one) into a scratch kilobyte of LDS that nothing reads, so
 // that the epilogue finds C in the caches.  With every tile reaching its
 // epilogue at the same moment (one tile per CU at 4096^3), C otherwise comes
 // from HBM in one burst with the output.
-template <int OP, int LAYOUT, int BL, bool PF>
+template <int OP, int LAYOUT, int BL, int MODE>
 __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __restrict__ A_vals,
                                                                  const char* __restrict__ meta,
                                                                  const char* __restrict__ B, void* C, int M, int N,
@@ -365,6 +367,7 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
                                                                  int tiles_n) {
   // One LDS object per stage.
   __shared__ __attribute__((aligned(1024))) char lS0[kLdsStage], lS1[kLdsStage], lS2[kLdsStage];
+  constexpr bool PF = MODE == 2, CACHED = MODE != 0;
   __shared__ __attribute__((aligned(1024))) char lPF[PF ? 1024 : 16];
   // (uniform selects; an array of LDS pointers would become a table in memory)
   auto st = [&](int i) -> SP24_LDS char* {
@@ -634,7 +637,7 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
         const int row = row_base + tm * 16 + (l >> 4) + 4 * q;
         const i32x4 c = cb[tm % kCPre][q];
         if (tm + kCPre < 8) cb[tm % kCPre][q] = cload(tm + kCPre, q);
-        if (row < M && col < N) store_out4_c<op_is_int(OP)>(C, (int64_t)row * N + col, col, v[q], c, ep);
+        if (row < M && col < N) store_out4_c<op_is_int(OP), CACHED>(C, (int64_t)row * N + col, col, v[q], c, ep);
       }
     }
     return;
@@ -660,8 +663,8 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
           const i32x2 c = cb[tm % kCPre][q];
           if (tm + kCPre < 8) cb[tm % kCPre][q] = cload(tm + kCPre, q);
           if (row < M && col < N) {
-            if (bf) store_out4_c16<true>(C, (int64_t)row * N + col, col, v[q], c, ep);
-            else store_out4_c16<false>(C, (int64_t)row * N + col, col, v[q], c, ep);
+            if (bf) store_out4_c16<true, CACHED>(C, (int64_t)row * N + col, col, v[q], c, ep);
+            else store_out4_c16<false, CACHED>(C, (int64_t)row * N + col, col, v[q], c, ep);
           }
         }
       }
@@ -684,7 +687,7 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
       if (row < M && col < N) {
         // streaming stores: the output is not re-read here, and letting it
         // allocate in the caches evicts the A and B data other tiles reuse
-        store_out4<op_is_int(OP)>(C, (int64_t)row * N + col, col, v, ep);
+        store_out4<op_is_int(OP), CACHED>(C, (int64_t)row * N + col, col, v, ep);
       }
     }
   }
@@ -999,13 +1002,29 @@ static hipError_t launch_op(const void* A_vals, const uint32_t* meta, const void
   // hidden by reading ahead in the epilogue itself, while the extra loads and
   // the C lines in the caches cost the main loop (fp16 8192^3, beta = 1:
   // 559 -> 569 us with it).
+  // When every tile runs at once the output stores are ordinary ones, which
+  // the caches absorb: bf16 4096^3 76.4 -> 74.7 us, fp16 4096^3 80.3 -> 76.7
+  // us (beta = 0); with more tiles streaming stores keep A and B in the
+  // caches for the tiles still running (fp16 8192^3: 515.6 against 547.0 us
+  // with ordinary stores).
+  // (MODE 1 and 2 are built for the K-blocked layout, the fast path, only.)
   const int64_t csize = ep.out == OUT_32 ? 4 : 2;
-  if (ep.beta != 0.0f && (int64_t)tiles_m * tiles_n <= kComputeUnits && (int64_t)kBM * N * csize < (1ll << 31))
-    hipLaunchKernelGGL((gemm_large8_kernel<OP, LAYOUT, BL, true>), dim3((unsigned)(tiles_m * tiles_n)),
-                       dim3(kThreads8), 0, stream, a, m, b, C, M, N, K, ep, tiles_m, tiles_n);
-  else
-    hipLaunchKernelGGL((gemm_large8_kernel<OP, LAYOUT, BL, false>), dim3((unsigned)(tiles_m * tiles_n)),
-                       dim3(kThreads8), 0, stream, a, m, b, C, M, N, K, ep, tiles_m, tiles_n);
+  const bool one_wave = LAYOUT == SP24_LAYOUT_KBLOCK && (int64_t)tiles_m * tiles_n <= kComputeUnits;
+  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kThreads8);
+  if constexpr (LAYOUT == SP24_LAYOUT_KBLOCK) {
+    if (one_wave && ep.beta != 0.0f && (int64_t)kBM * N * csize < (1ll << 31)) {
+      hipLaunchKernelGGL((gemm_large8_kernel<OP, LAYOUT, BL, 2>), grid, block, 0, stream, a, m, b, C, M, N, K, ep,
+                         tiles_m, tiles_n);
+      return hipGetLastError();
+    }
+    if (one_wave) {
+      hipLaunchKernelGGL((gemm_large8_kernel<OP, LAYOUT, BL, 1>), grid, block, 0, stream, a, m, b, C, M, N, K, ep,
+                         tiles_m, tiles_n);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_large8_kernel<OP, LAYOUT, BL, 0>), grid, block, 0, stream, a, m, b, C, M, N, K, ep,
+                     tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -117,64 +117,76 @@ struct Epilogue {
   int out;            // OutType
 };
 
+// The product's output stores (CACHED is a compile-time choice: with a
+// run-time one the compiler merges the two stores of the same value and
+// keeps the ordinary one).  Streaming by default: while other tiles are still
+// reading A and B, letting the output allocate in the caches evicts them.
+// When every tile runs at once nothing is read after the epilogues, and
+// ordinary stores let the caches absorb the burst of all outputs.
+template <bool CACHED, typename T>
+__device__ __forceinline__ void put(T v, T* p) {
+  if constexpr (CACHED) *p = v;
+  else __builtin_nontemporal_store(v, p);
+}
+
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // Four consecutive outputs of one row at element offset o, column col
 // (col % 4 == 0, all four inside N).  v = the fp32 accumulators.
-template <bool INT>
+template <bool INT, bool CACHED>
 __device__ __forceinline__ void store_out4(void* C, int64_t o, int col, f32x4 v, const Epilogue& ep) {
   if constexpr (INT) {
     i32x4 d = __builtin_bit_cast(i32x4, v);
     if (ep.beta != 0.0f) d += __builtin_nontemporal_load((const i32x4*)((const int*)C + o));
-    __builtin_nontemporal_store(d, (i32x4*)((int*)C + o));
+    put<CACHED>(d, (i32x4*)((int*)C + o));
   } else {
     f32x4 d = v * ep.alpha;
     if (ep.out == OUT_32) {
       if (ep.beta != 0.0f) d += ep.beta * __builtin_nontemporal_load((const f32x4*)((const float*)C + o));
       if (ep.bias) d += *(const f32x4*)(ep.bias + col);
-      __builtin_nontemporal_store(d, (f32x4*)((float*)C + o));
+      put<CACHED>(d, (f32x4*)((float*)C + o));
     } else if (ep.out == OUT_F16) {
       f16x4* p = (f16x4*)((_Float16*)C + o);
       if (ep.beta != 0.0f) d += ep.beta * __builtin_convertvector(__builtin_nontemporal_load(p), f32x4);
       if (ep.bias) d += *(const f32x4*)(ep.bias + col);
-      __builtin_nontemporal_store(__builtin_convertvector(d, f16x4), p);
+      put<CACHED>(__builtin_convertvector(d, f16x4), p);
     } else {
       bf16x4* p = (bf16x4*)((__bf16*)C + o);
       if (ep.beta != 0.0f) d += ep.beta * __builtin_convertvector(__builtin_nontemporal_load(p), f32x4);
       if (ep.bias) d += *(const f32x4*)(ep.bias + col);
-      __builtin_nontemporal_store(__builtin_convertvector(d, bf16x4), p);
+      put<CACHED>(__builtin_convertvector(d, bf16x4), p);
     }
   }
 }
 
 // store_out4 for a 32-bit output with beta != 0, with the four C values
 // (their bits) already read: the same arithmetic.
-template <bool INT>
+template <bool INT, bool CACHED>
 __device__ __forceinline__ void store_out4_c(void* C, int64_t o, int col, f32x4 v, i32x4 c, const Epilogue& ep) {
   if constexpr (INT) {
-    __builtin_nontemporal_store(__builtin_bit_cast(i32x4, v) + c, (i32x4*)((int*)C + o));
+    put<CACHED>(__builtin_bit_cast(i32x4, v) + c, (i32x4*)((int*)C + o));
   } else {
     f32x4 d = v * ep.alpha;
     d += ep.beta * __builtin_bit_cast(f32x4, c);
     if (ep.bias) d += *(const f32x4*)(ep.bias + col);
-    __builtin_nontemporal_store(d, (f32x4*)((float*)C + o));
+    put<CACHED>(d, (f32x4*)((float*)C + o));
   }
 }
 
 // store_out4 for a 16-bit output (BF: bfloat16, else fp16) with beta != 0,
 // with the four C values (their bits) already read: the same arithmetic.
-template <bool BF>
+template <bool BF, bool CACHED>
 __device__ __forceinline__ void store_out4_c16(void* C, int64_t o, int col, f32x4 v, i32x2 c, const Epilogue& ep) {
   f32x4 d = v * ep.alpha;
   if constexpr (BF) {
     d += ep.beta * __builtin_convertvector(__builtin_bit_cast(bf16x4, c), f32x4);
     if (ep.bias) d += *(const f32x4*)(ep.bias + col);
-    __builtin_nontemporal_store(__builtin_convertvector(d, bf16x4), (bf16x4*)((__bf16*)C + o));
+    put<CACHED>(__builtin_convertvector(d, bf16x4), (bf16x4*)((__bf16*)C + o));
   } else {
     d += ep.beta * __builtin_convertvector(__builtin_bit_cast(f16x4, c), f32x4);
     if (ep.bias) d += *(const f32x4*)(ep.bias + col);
-    __builtin_nontemporal_store(__builtin_convertvector(d, f16x4), (f16x4*)((_Float16*)C + o));
+    put<CACHED>(__builtin_convertvector(d, f16x4), (f16x4*)((_Float16*)C + o));
   }
 }
 
