@@ -420,19 +420,21 @@ def test_gemm_out16_bias(pkg, out, a_type, b_type, N, with_bias, b_layout):
     assert np.array_equal(D.view(torch.int16).cpu().numpy().view(np.uint16)[far], exp_bits)
 
 
+@pytest.mark.parametrize("k_tail", [0, 32])
 @pytest.mark.parametrize("b_layout", [KN, NK])
 @pytest.mark.parametrize("out", [None, wl.F16, wl.BF16])
 @pytest.mark.parametrize("a_type,b_type", [(wl.F16, wl.F16), (wl.I8, wl.I8), (wl.E5M2, wl.E4M3)])
-def test_gemm_beta_c_read_ahead_window(pkg, a_type, b_type, out, b_layout):
+def test_gemm_beta_c_read_ahead_window(pkg, a_type, b_type, out, b_layout, k_tail):
     """beta != 0 on a grid of at most one tile per compute unit, where the
-    product reads the tile's C ahead during its last 32 load steps: 40 k-steps
-    (the window starts inside the loop), ragged M and N (rows of the last
-    pieces past M, columns past N), 32-bit and 16-bit C (one or two tile rows
-    per piece); every output against the oracle."""
+    product reads the tile's C ahead during its last 32 load steps: 40 or 41
+    k-steps (the window starts inside the loop; with k_tail the last step is
+    partial), ragged M and N (rows of the last pieces past M, columns past
+    N), 32-bit and 16-bit C (one or two tile rows per piece); every output
+    against the oracle."""
     if a_type == wl.I8 and out is not None:
         pytest.skip("int8 has a 32-bit output only")
-    M, N = 700, 528  # N % 16 == 0: 8-bit B stored K x N above N = 64 needs it
-    K = 40 * (64 if wl.ESIZE[a_type] == 2 else 128)
+    M, N = 701, 528  # N % 16 == 0: 8-bit B stored K x N above N = 64 needs it
+    K = 40 * (64 if wl.ESIZE[a_type] == 2 else 128) + k_tail
     _say(f"gemm beta read-ahead window a={a_type} out={out} b_layout={b_layout} K={K}")
     c = wl.random_case(53, M, N, K, a_type, b_type, beta=1.0)
     vals, meta = oracle.prune_compress(c.A, a_type)
