@@ -157,7 +157,7 @@ def compress_launch_shape(M, K, es, layout):
         nblk, row_tiles = -(-K // (64 if es == 2 else 128)), -(-M // 128)
         if es == 2:
             nb = 2 if row_tiles * (-(-nblk // 2)) >= 1024 else 1
-            return row_tiles * (-(-nblk // nb)), 256
+            return row_tiles * (-(-nblk // nb)), 512
         return row_tiles * nblk, 512
     return -(-(M * K * es // 16) // 1024), 256
 
