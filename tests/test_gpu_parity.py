@@ -420,33 +420,38 @@ def test_gemm_out16_bias(pkg, out, a_type, b_type, N, with_bias, b_layout):
     assert np.array_equal(D.view(torch.int16).cpu().numpy().view(np.uint16)[far], exp_bits)
 
 
+@pytest.mark.parametrize("beta_zero", [False, True])
 @pytest.mark.parametrize("k_tail", [0, 32])
 @pytest.mark.parametrize("b_layout", [KN, NK])
 @pytest.mark.parametrize("out", [None, wl.F16, wl.BF16])
 @pytest.mark.parametrize("a_type,b_type", [(wl.F16, wl.F16), (wl.I8, wl.I8), (wl.E5M2, wl.E4M3)])
-def test_gemm_beta_c_read_ahead_window(pkg, a_type, b_type, out, b_layout, k_tail):
-    """beta != 0 on a grid of at most one tile per compute unit, where the
-    product reads the tile's C ahead during its last 32 load steps: 40 or 41
-    k-steps (the window starts inside the loop; with k_tail the last step is
-    partial), ragged M and N (rows of the last pieces past M, columns past
-    N), 32-bit and 16-bit C (one or two tile rows per piece); every output
+def test_gemm_one_wave_modes(pkg, a_type, b_type, out, b_layout, k_tail, beta_zero):
+    """A grid of at most one tile per compute unit, where the product stores
+    its output with ordinary stores and, with beta != 0, reads the tile's C
+    ahead during its last 32 load steps: 40 or 41 k-steps (the window starts
+    inside the loop; with k_tail the last step is partial), ragged M and N
+    (rows of the last pieces past M, columns past N), 32-bit and 16-bit C
+    (one or two tile rows per piece), beta != 0 and beta == 0; every output
     against the oracle."""
     if a_type == wl.I8 and out is not None:
         pytest.skip("int8 has a 32-bit output only")
     M, N = 701, 528  # N % 16 == 0: 8-bit B stored K x N above N = 64 needs it
     K = 40 * (64 if wl.ESIZE[a_type] == 2 else 128) + k_tail
-    _say(f"gemm beta read-ahead window a={a_type} out={out} b_layout={b_layout} K={K}")
+    _say(f"gemm one-wave modes a={a_type} out={out} b_layout={b_layout} K={K} beta_zero={beta_zero}")
     c = wl.random_case(53, M, N, K, a_type, b_type, beta=1.0)
     vals, meta = oracle.prune_compress(c.A, a_type)
     if out is None:
         alpha, beta = (1.0, 1.0) if a_type == wl.I8 else (0.75, -1.25)
+        if beta_zero:
+            beta = 0.0
         check_gemm_full(pkg, vals, meta, a_type, c.B, b_type, c.C, alpha, beta, KBLOCK, b_layout)
         return
+    beta = 0.0 if beta_zero else -1.25
     C16 = torch.from_numpy(c.C).to(OUT_T[out])
     C32 = C16.to(torch.float32).numpy()
-    D = run_gemm_ex(pkg, vals, meta, a_type, c.B, b_type, C16.to(DEV), OUT_T[out], None, 0.75, -1.25, b_layout)
+    D = run_gemm_ex(pkg, vals, meta, a_type, c.B, b_type, C16.to(DEV), OUT_T[out], None, 0.75, beta, b_layout)
     got = oracle.decode(D.view(torch.int16).cpu().numpy().view(np.uint16), out)
-    ref, S = oracle.gemm_f64(vals, meta, a_type, c.B, b_type, C32, alpha=0.75, beta=-1.25)
+    ref, S = oracle.gemm_f64(vals, meta, a_type, c.B, b_type, C32, alpha=0.75, beta=beta)
     err = np.abs(got - ref)
     assert (err <= 1e-4 * S + 1e-6 + grid_spacing(ref, out)).all(), f"worst {np.max(err - 1e-4 * S):.3g}"
 
