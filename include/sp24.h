@@ -185,7 +185,9 @@ int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, 
  *                 N * sizeof(b_type) <= 16 MiB - 2 (so 128 rows of B stay
  *                 below 2 GiB), for SP24_B_NK 256 * K * sizeof(b_type) <
  *                 2 GiB and, for the ROW layout, 256 * K/2 * sizeof(a_type)
- *                 < 2 GiB (K <= 8388606 for 16-bit types).
+ *                 < 2 GiB (K <= 8388606 for 16-bit types); for K > 0 and
+ *                 N > 64, fewer than 2^23 output tiles of 256 x 256
+ *                 (always so for an output that fits in device memory).
  *                 M == 0 or N == 0: nothing is enqueued.  K == 0: D = beta*C.
  *   alpha, beta   float scalars.  For int8: alpha must be 1, beta 0 or 1.
  *   workspace     may be NULL when sp24_gemm_workspace_bytes() == 0.

@@ -217,9 +217,8 @@ def gemm(A_vals, meta, B, C=None, alpha: float = 1.0, beta: float = 0.0, a_type:
     int8 inputs) is the type of C / D, taken from C when it is given.
     ``bias``: optional length-N float32 tensor added to every row (calls
     sp24_gemm_ex).  ``workspace``: optional uint8 device tensor of at least
-    sp24_gemm_workspace_bytes() bytes, zero-filled before its first use (the
-    library leaves its counters at zero); allocated per call when needed and
-    not given.  Returns C."""
+    sp24_gemm_workspace_bytes() bytes, which is 0 for every problem at
+    present; allocated per call when needed and not given.  Returns C."""
     import torch
     if a_type is None:
         a_type = dtype_code(A_vals.dtype)
@@ -257,9 +256,8 @@ def gemm(A_vals, meta, B, C=None, alpha: float = 1.0, beta: float = 0.0, a_type:
             raise ValueError("A_vals, meta and C must be contiguous")
     if bias is not None and (bias.dtype != torch.float32 or not bias.is_contiguous() or bias.numel() != N):
         raise ValueError("bias must be a contiguous float32 tensor of N values")
-    # the small-N product splits K over workgroups and combines their partial
-    # tiles through a workspace whose counters start at zero (and are left
-    # at zero): a fresh zero-filled buffer per call here
+    # a workspace only if the library asks for one (no kernel uses one at
+    # present)
     ws_bytes = sp24_gemm_workspace_bytes(M, N, K, a_type, b_type)
     if workspace is None and ws_bytes:
         workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=B.device)

@@ -121,6 +121,9 @@ int sp24_gemm_ex(const void* A_vals, const uint32_t* meta, int a_type, int layou
   if ((uint64_t)N * eb * 128 > kTileBytesMax) return SP24_ERR_UNSUPPORTED;
   if (layout == SP24_LAYOUT_ROW && (uint64_t)(K / 2) * ea * 256 > kTileBytesMax) return SP24_ERR_UNSUPPORTED;
   if (b_layout == SP24_B_NK && (uint64_t)K * eb * 256 > kTileBytesMax) return SP24_ERR_UNSUPPORTED;
+  // one workgroup of 512 threads per 256 x 256 output tile, in one grid
+  // dimension of fewer than 2^32 work-items (an output of over 2^39 elements)
+  if (K > 0 && N > 64 && ((M + 255) / 256) * ((N + 255) / 256) >= (1ll << 23)) return SP24_ERR_UNSUPPORTED;
   if (op == sp24::OP_I8 && (alpha != 1.0f || (beta != 0.0f && beta != 1.0f))) return SP24_ERR_UNSUPPORTED;
   if (workspace_bytes < sp24_gemm_workspace_bytes(M, N, K, a_type, b_type)) return SP24_ERR_INVALID_VALUE;
   (void)workspace;

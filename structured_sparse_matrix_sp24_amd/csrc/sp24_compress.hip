@@ -201,7 +201,7 @@ constexpr int kKbBlocks16 = 2, kKbThreads16 = 512, kKbThreads8 = 512;
 template <int ES, bool INT, int NB, int T>
 __global__ __launch_bounds__(T) void prune_compress_kblock_kernel(const char* __restrict__ A, char* __restrict__ vals,
                                                                   char* __restrict__ meta, int64_t M, int64_t K,
-                                                                  uint32_t nblk) {
+                                                                  uint32_t nblk, uint32_t wg0) {
   constexpr int MB = ES == 2 ? 8 : 16;         // metadata bytes per row per block
   constexpr int CE = 16 / ES;                   // dense elements per chunk
   constexpr int GB = 128 * MB;                  // metadata bytes of one 128-row group per block
@@ -210,8 +210,9 @@ __global__ __launch_bounds__(T) void prune_compress_kblock_kernel(const char* __
   constexpr int NR = 128 / RPR;                 // load rounds
   __shared__ __attribute__((aligned(16))) char lmeta[NB * GB];
   const uint32_t nwb = (nblk + NB - 1) / NB;
-  const int64_t b0 = (int64_t)(blockIdx.x % nwb) * NB;
-  const uint32_t rt = blockIdx.x / nwb;
+  const uint32_t g = wg0 + blockIdx.x;  // workgroup index over all pieces of the launch
+  const int64_t b0 = (int64_t)(g % nwb) * NB;
+  const uint32_t rt = g / nwb;
   const int64_t Mp = (M + 127) / 128 * 128;
   const int cc = threadIdx.x % CPR;             // chunk in the tile row
   const int bi = cc / 8, c = cc % 8;            // block in the tile, chunk in the block
@@ -290,30 +291,36 @@ hipError_t launch_prune_compress(const void* A, void* vals, uint32_t* meta, int6
     const int nb_per_wg =
         (es == 2 && row_tiles * ((nblk + kKbBlocks16 - 1) / kKbBlocks16) >= kKbMinWorkgroups) ? kKbBlocks16 : 1;
     const int64_t nwb = (nblk + nb_per_wg - 1) / nb_per_wg;
-    if (row_tiles * nwb > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(row_tiles * nwb));
+    const int64_t total = row_tiles * nwb;
+    if (total > 0x7FFFFFFFll) return hipErrorInvalidValue;
     const char* a = static_cast<const char*>(A);
     char* v = static_cast<char*>(vals);
     char* m = reinterpret_cast<char*>(meta);
     const uint32_t nb = (uint32_t)nblk;
-    if (es == 2 && nb_per_wg == kKbBlocks16)
-      hipLaunchKernelGGL((prune_compress_kblock_kernel<2, false, kKbBlocks16, kKbThreads16>), grid, block, 0, stream,
-                         a, v, m, M, K, nb);
-    else if (es == 2)
-      hipLaunchKernelGGL((prune_compress_kblock_kernel<2, false, 1, kKbThreads16>), grid, block, 0, stream, a, v, m,
-                         M, K, nb);
-    else if (is_int)
-      hipLaunchKernelGGL((prune_compress_kblock_kernel<1, true, 1, kKbThreads8>), grid, block, 0, stream, a, v, m, M,
-                         K, nb);
-    else
-      hipLaunchKernelGGL((prune_compress_kblock_kernel<1, false, 1, kKbThreads8>), grid, block, 0, stream, a, v, m,
-                         M, K, nb);
-    return hipGetLastError();
+    for (int64_t first = 0; first < total; first += kMaxLaunchWorkgroups) {
+      const dim3 grid((unsigned)(total - first < kMaxLaunchWorkgroups ? total - first : kMaxLaunchWorkgroups));
+      const uint32_t g0 = (uint32_t)first;
+      if (es == 2 && nb_per_wg == kKbBlocks16)
+        hipLaunchKernelGGL((prune_compress_kblock_kernel<2, false, kKbBlocks16, kKbThreads16>), grid, block, 0,
+                           stream, a, v, m, M, K, nb, g0);
+      else if (es == 2)
+        hipLaunchKernelGGL((prune_compress_kblock_kernel<2, false, 1, kKbThreads16>), grid, block, 0, stream, a, v,
+                           m, M, K, nb, g0);
+      else if (is_int)
+        hipLaunchKernelGGL((prune_compress_kblock_kernel<1, true, 1, kKbThreads8>), grid, block, 0, stream, a, v, m,
+                           M, K, nb, g0);
+      else
+        hipLaunchKernelGGL((prune_compress_kblock_kernel<1, false, 1, kKbThreads8>), grid, block, 0, stream, a, v,
+                           m, M, K, nb, g0);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   const int64_t nchunks = M * K * es / 16;
   const int64_t per_block = (int64_t)kCompressThreads * kCompressUnroll;
   const int64_t blocks = (nchunks + per_block - 1) / per_block;
-  if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+  if (blocks * kCompressThreads > 0xFFFFFFFFll) return hipErrorInvalidValue;  // A > 256 GiB
   const dim3 grid((unsigned)blocks);
   const i32x4* a = static_cast<const i32x4*>(A);
   i32x2* v = static_cast<i32x2*>(vals);

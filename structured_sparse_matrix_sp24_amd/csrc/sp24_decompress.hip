@@ -82,12 +82,13 @@ template <int ES, int NB, int T>
 __global__ __launch_bounds__(T) void decompress_kblock_kernel(const char* __restrict__ vals,
                                                                const char* __restrict__ meta,
                                                                char* __restrict__ A, int64_t M, int64_t K,
-                                                               uint32_t nblk) {
+                                                               uint32_t nblk, uint32_t wg0) {
   constexpr int MB = ES == 2 ? 8 : 16, CE = 16 / ES;
   constexpr int CPR = 8 * NB, RPR = T / CPR, NR = 128 / RPR;
   const uint32_t nwb = (nblk + NB - 1) / NB;
-  const int64_t b = (int64_t)(blockIdx.x % nwb) * NB + (threadIdx.x % CPR) / 8;
-  const uint32_t rt = blockIdx.x / nwb;
+  const uint32_t g = wg0 + blockIdx.x;  // workgroup index over all pieces of the launch
+  const int64_t b = (int64_t)(g % nwb) * NB + (threadIdx.x % CPR) / 8;
+  const uint32_t rt = g / nwb;
   const int64_t Mp = (M + 127) / 128 * 128;
   const int c = threadIdx.x & 7;
   const int64_t kcol = b * (8 * CE) + (int64_t)c * CE;
@@ -202,23 +203,33 @@ hipError_t launch_decompress(const void* vals, const uint32_t* meta, void* A, in
     // workgroup while that leaves at least 1024 workgroups; 512 threads
     const int nb = es == 2 && row_tiles * ((nblk + 1) / 2) >= 1024 ? 2 : 1;
     const int64_t nwb = (nblk + nb - 1) / nb;
-    if (row_tiles * nwb > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(row_tiles * nwb)), blk(kDecKbThreads);
+    const int64_t total = row_tiles * nwb;
+    if (total > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    const dim3 blk(kDecKbThreads);
     const char* v = static_cast<const char*>(vals);
     const char* m = reinterpret_cast<const char*>(meta);
     char* a = static_cast<char*>(A);
     const uint32_t n = (uint32_t)nblk;
-    if (es == 2 && nb == 2)
-      hipLaunchKernelGGL((decompress_kblock_kernel<2, 2, kDecKbThreads>), grid, blk, 0, stream, v, m, a, M, K, n);
-    else if (es == 2)
-      hipLaunchKernelGGL((decompress_kblock_kernel<2, 1, kDecKbThreads>), grid, blk, 0, stream, v, m, a, M, K, n);
-    else
-      hipLaunchKernelGGL((decompress_kblock_kernel<1, 1, kDecKbThreads>), grid, blk, 0, stream, v, m, a, M, K, n);
-    return hipGetLastError();
+    for (int64_t first = 0; first < total; first += kMaxLaunchWorkgroups) {
+      const dim3 grid((unsigned)(total - first < kMaxLaunchWorkgroups ? total - first : kMaxLaunchWorkgroups));
+      const uint32_t g0 = (uint32_t)first;
+      if (es == 2 && nb == 2)
+        hipLaunchKernelGGL((decompress_kblock_kernel<2, 2, kDecKbThreads>), grid, blk, 0, stream, v, m, a, M, K, n,
+                           g0);
+      else if (es == 2)
+        hipLaunchKernelGGL((decompress_kblock_kernel<2, 1, kDecKbThreads>), grid, blk, 0, stream, v, m, a, M, K, n,
+                           g0);
+      else
+        hipLaunchKernelGGL((decompress_kblock_kernel<1, 1, kDecKbThreads>), grid, blk, 0, stream, v, m, a, M, K, n,
+                           g0);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   const int64_t nchunks = M * K * es / 16;
   const int64_t blocks = (nchunks + kDecThreads * kDecUnroll - 1) / (kDecThreads * kDecUnroll);
-  if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+  if (blocks * kDecThreads > 0xFFFFFFFFll) return hipErrorInvalidValue;  // A > 256 GiB
   const i32x2* v = static_cast<const i32x2*>(vals);
   const uint8_t* m = reinterpret_cast<const uint8_t*>(meta);
   i32x4* a = static_cast<i32x4*>(A);

@@ -685,8 +685,9 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
       const f32x4 v = *(const SP24_LDS f32x4*)(scr + rr * kScrRow + (l & 15) * 4);
       const int row = row_base + tm * 16 + rr;
       if (row < M && col < N) {
-        // streaming stores: the output is not re-read here, and letting it
-        // allocate in the caches evicts the A and B data other tiles reuse
+        // streaming stores unless every tile runs at once: the output is not
+        // re-read here, and letting it allocate in the caches evicts the A
+        // and B data other tiles reuse
         store_out4<op_is_int(OP), CACHED>(C, (int64_t)row * N + col, col, v, ep);
       }
     }
@@ -733,7 +734,7 @@ template <int OP, int LAYOUT, int D, int BL>
 __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const char* __restrict__ A_vals,
                                                                         const char* __restrict__ meta,
                                                                         const char* __restrict__ B, void* C, int M,
-                                                                        int N, int K, Epilogue ep) {
+                                                                        int N, int K, Epilogue ep, int tile0) {
   constexpr int KS = op_kstep(OP), ES = op_esize(OP), MB = meta_step_bytes<OP>();
   constexpr int SLOT = small_bslice<D>();
   constexpr int NT = 8 / D;  // column tiles computed: the slice of D = 8, 4, 2 holds N <= 16, 32, 64
@@ -747,6 +748,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
   // 4096 x 16 x 4096).
   int tile = blockIdx.x;
   if ((gridDim.x & 7) == 0) tile = (tile & 7) * (gridDim.x >> 3) + (tile >> 3);
+  tile += tile0;  // first tile of this piece of the launch
   const int m0 = tile * 16;
   const int ga = l >> 4, gb = l >> 4, s = l & 15;
   const int nt = (N + 15) >> 4;
@@ -792,7 +794,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
   // all ask for the same few B lines at once, each one starts its waves'
   // step lists at a different point (a fixed rotation per workgroup: the
   // summation order, and so the result, does not depend on timing).
-  const int rot = nw > 0 ? (int)(blockIdx.x % (unsigned)nw) : 0;
+  const int rot = nw > 0 ? (int)((blockIdx.x + (unsigned)tile0) % (unsigned)nw) : 0;
 
   // Global k-step of this wave's local step j (local steps past nw map to
   // steps past the end, whose loads read nothing).
@@ -956,16 +958,18 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gemm_smalln_kernel(const cha
 }
 
 // ---- K == 0: D = beta * C (+ bias), in the output type -----------------------
+// (grid-stride: an output of any size takes one launch of a bounded grid)
 template <bool INT>
 __global__ void scale_c_kernel(void* C, int64_t n, int N, Epilogue ep) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  if constexpr (INT) {
-    int* D = static_cast<int*>(C);
-    D[i] = ep.beta != 0.0f ? D[i] : 0;
-  } else {
-    // alpha * (empty sum) = +0, then beta * C and the bias as in store_out1
-    store_out1<false>(C, i, (int)(i % N), 0.0f, ep);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    if constexpr (INT) {
+      int* D = static_cast<int*>(C);
+      D[i] = ep.beta != 0.0f ? D[i] : 0;
+    } else {
+      // alpha * (empty sum) = +0, then beta * C and the bias as in store_out1
+      store_out1<false>(C, i, (int)(i % N), 0.0f, ep);
+    }
   }
 }
 
@@ -979,20 +983,30 @@ static hipError_t launch_op(const void* A_vals, const uint32_t* meta, const void
     const int64_t n = (int64_t)M * N;
     Epilogue e0 = ep;
     e0.alpha = 0.0f;  // D = beta * C (+ bias) whatever alpha is, as BLAS does for K == 0
-    hipLaunchKernelGGL((scale_c_kernel<op_is_int(OP)>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, C, n,
-                       N, e0);
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL((scale_c_kernel<op_is_int(OP)>), dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256),
+                       0, stream, C, n, N, e0);
     return hipGetLastError();
   }
   if (N <= 64) {
-    const dim3 grid((unsigned)((M + 15) / 16)), block(kSmallWaves * 64);
+    const int tiles = (int)(((int64_t)M + 15) / 16);
+    const dim3 block(kSmallWaves * 64);
     const int64_t slice = (int64_t)op_kstep(OP) * N * op_esize(OP);  // B bytes per k-step
-    if (slice <= small_bslice<8>())
-      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 8, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep);
-    else if (slice <= small_bslice<4>())
-      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 4, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep);
-    else
-      hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 2, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep);
-    return hipGetLastError();
+    for (int first = 0; first < tiles; first += (int)kMaxLaunchWorkgroups) {
+      const dim3 grid((unsigned)(tiles - first < (int)kMaxLaunchWorkgroups ? tiles - first : (int)kMaxLaunchWorkgroups));
+      if (slice <= small_bslice<8>())
+        hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 8, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep,
+                           first);
+      else if (slice <= small_bslice<4>())
+        hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 4, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep,
+                           first);
+      else
+        hipLaunchKernelGGL((gemm_smalln_kernel<OP, LAYOUT, 2, BL>), grid, block, 0, stream, a, m, b, C, M, N, K, ep,
+                           first);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
   // C read ahead during the main loop only when every tile runs at once (at

@@ -70,6 +70,12 @@ __device__ __forceinline__ i32x4 smfmac16(i32x4 acc, i32x4 a, i32x8 b, int idx) 
   }
 }
 
+// A dispatch counts its work-items in 32 bits per grid dimension, so a grid
+// of 512-thread workgroups must stay below 2^23 of them.  Kernels whose
+// workgroup count grows with the problem are launched in pieces of at most
+// this many workgroups; each piece passes the index of its first workgroup.
+static constexpr uint32_t kMaxLaunchWorkgroups = 1u << 18;
+
 // ---- buffer resources: raw byte-addressed, hardware range-checked ----------
 // Reads at offsets >= num_records return zeros, which is how ragged edges and
 // the K tail are handled without branches.

@@ -609,6 +609,69 @@ def test_operands_past_4gib(pkg):
         assert (err <= 1e-4 * S + 1e-6).all(), f"rows {rows}: worst ratio {np.max(err / (S + 1e-30)):.3g}"
 
 
+def test_launches_in_pieces(pkg):
+    """Problems that need more workgroups than one launch is given (2^18; a
+    dispatch counts its work-items in 32 bits): int8 A of 2^25 + 200 rows x
+    128 (4.3 GB), so the K-blocked compress and decompress (one 128-row
+    group per workgroup) take two launches, and the small-N product (16 rows
+    per workgroup) nine.  Compared with the oracle on whole 128-row groups on
+    both sides of the compress pieces' boundary and the ragged end, and on
+    the rows on both sides of every boundary between product pieces."""
+    M, K, N = (1 << 25) + 200, 128, 8
+    dtype = wl.I8
+    _say(f"launches in pieces: M={M} K={K} N={N}")
+    A = wl.small_int_bits((M, K), dtype, 61, -127, 127)
+    B = wl.small_int_bits((K, N), dtype, 62, -127, 127)
+    At = to_dev(A, dtype)
+    vals, meta = pkg.prune_compress(At, dtype, KBLOCK)
+    del At
+    torch.cuda.synchronize()
+    groups = [(0, 128), ((1 << 25) - 128, 128), (1 << 25, 128), ((1 << 25) + 128, 72)]
+    for r0, g in groups:
+        ov, om = oracle.prune_compress(A[r0:r0 + g], dtype)
+        ev, em = row_to_kblock(ov, om, dtype)
+        assert np.array_equal(meta[:, r0:r0 + 128, :].cpu().numpy().view(np.uint32), em), f"metadata of rows {r0}.."
+        assert np.array_equal(to_host_bits(vals[:, r0:r0 + g, :], dtype).view(ev.dtype), ev), f"values of rows {r0}.."
+    _say("launches in pieces: decompress")
+    Ad = pkg.decompress(vals, meta, K, dtype, KBLOCK)
+    torch.cuda.synchronize()
+    for r0, g in groups:
+        ov, om = oracle.prune_compress(A[r0:r0 + g], dtype)
+        assert np.array_equal(to_host_bits(Ad[r0:r0 + g], dtype), oracle.decompress(ov, om, dtype)), f"rows {r0}.."
+    del Ad
+    _say("launches in pieces: small-N product")
+    D = pkg.gemm(vals, meta, to_dev(B, dtype), None, a_type=dtype, b_type=dtype, layout=KBLOCK)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(p * (1 << 22) - 16, p * (1 << 22) + 16) for p in range(1, 9)] +
+                          [np.arange(0, 16), np.arange(M - 40, M)])
+    ov, om = oracle.prune_compress(A[rows], dtype)
+    assert np.array_equal(D[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.int64),
+                          oracle.gemm_i64(ov, om, B))
+
+
+def test_gemm_K_zero_past_2e32_elements(pkg):
+    """K == 0 (D = beta * C) on an fp16 output of more than 2^32 elements
+    (8.6 GB): the kernel covers it with a bounded grid that walks the whole
+    output.  beta = 2 on small integers is exact, so every checked element
+    equals 2 * C exactly: whole rows at the start, on both sides of element
+    2^32 and at the end."""
+    M, N = (1 << 16) + 8, 1 << 16
+    _say(f"K = 0 with M={M} N={N}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(71)
+    C = torch.randint(-1000, 1001, (M, N), dtype=torch.int16, device=DEV, generator=g).to(torch.float16)
+    rows = torch.tensor([0, 1, (1 << 16) - 1, 1 << 16, (1 << 16) + 1, M - 1], device=DEV)
+    before = C[rows].float().cpu().numpy().astype(np.float64)
+    vs, ms = pkg.compressed_shapes(M, 0, pkg.SP24_F16, KBLOCK)
+    V = torch.empty(vs, dtype=torch.float16, device=DEV)
+    Mt = torch.empty(ms, dtype=torch.int32, device=DEV)
+    B = torch.empty((0, N), dtype=torch.float16, device=DEV)
+    pkg.gemm(V, Mt, B, C, beta=2.0, layout=KBLOCK)
+    torch.cuda.synchronize()
+    after = C[rows].float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(after, 2.0 * before)
+
+
 def test_gemm_gpu_compressed_input(pkg):
     """Compress on the GPU and multiply the result directly."""
     _say("gemm on GPU-compressed input")
