@@ -136,7 +136,8 @@ size_t sp24_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int a_type, in
  *   A       in:  M x K elements of `dtype`.
  *   A_vals  out: sp24_values_bytes(M, K, dtype, layout) bytes.
  *   meta    out: sp24_meta_bytes(M, K, dtype, layout) bytes.
- *   M, K    M >= 0, K >= 0, K % 32 == 0.  M == 0 or K == 0 enqueues nothing.
+ *   M, K    0 <= M, K <= 2^31 - 1, K % 32 == 0.  M == 0 or K == 0 enqueues
+ *           nothing.
  *   layout  SP24_LAYOUT_ROW or SP24_LAYOUT_KBLOCK.
  * Errors: INVALID_VALUE (shape, null pointer with nonzero size, A overlapping
  * an output), UNSUPPORTED (unknown dtype or layout), MISALIGNED (pointer not
@@ -180,8 +181,8 @@ int sp24_prune_compress(const void* A, void* A_vals, uint32_t* meta, int64_t M, 
  *                 N x K (SP24_B_NK), as `b_layout` says.
  *   C             in/out: M x N float32 (int32 for int8 x int8).  Not read
  *                 when beta == 0 (NaN there does not propagate).
- *   M, N, K       >= 0, K % 32 == 0, N % 8 == 0 (and, for 8-bit B stored
- *                 K x N with N > 64, N % 16 == 0),
+ *   M, N, K       0 <= M, N, K <= 2^31 - 1, K % 32 == 0, N % 8 == 0 (and,
+ *                 for 8-bit B stored K x N with N > 64, N % 16 == 0),
  *                 N * sizeof(b_type) <= 16 MiB - 2 (so 128 rows of B stay
  *                 below 2 GiB), for SP24_B_NK 256 * K * sizeof(b_type) <
  *                 2 GiB and, for the ROW layout, 256 * K/2 * sizeof(a_type)
@@ -239,6 +240,7 @@ int sp24_gemm_ex(const void* A_vals, const uint32_t* meta, int a_type, int layou
  *   A_vals, meta  in: compressed A in `layout` (sizes as for
  *                 sp24_prune_compress).
  *   A             out: M x K elements of `dtype`, row-major.
+ *   M, K          as for sp24_prune_compress.
  * Errors: INVALID_VALUE (shape, null pointer, A overlapping an input),
  * UNSUPPORTED (dtype or layout), MISALIGNED, LAUNCH.
  */
