@@ -456,6 +456,21 @@ def test_gemm_one_wave_modes(pkg, a_type, b_type, out, b_layout, k_tail, beta_ze
     assert (err <= 1e-4 * S + 1e-6 + grid_spacing(ref, out)).all(), f"worst {np.max(err - 1e-4 * S):.3g}"
 
 
+@pytest.mark.parametrize("M", [4096, 4104])
+@pytest.mark.parametrize("a_type,b_type", [(wl.F16, wl.F16), (wl.I8, wl.I8)])
+def test_gemm_tile_count_boundary(pkg, a_type, b_type, M):
+    """Either side of one tile per compute unit: 4096 x 4096 is 256 output
+    tiles of 256 x 256 (ordinary output stores, C read ahead in the main
+    loop), 4104 x 4096 is 272 (streaming stores, C read in the epilogue);
+    beta != 0, every output against the oracle."""
+    N, K = 4096, 96 if wl.ESIZE[a_type] == 2 else 160
+    _say(f"gemm tile-count boundary a={a_type} M={M} N={N} K={K}")
+    c = wl.random_case(57, M, N, K, a_type, b_type, beta=1.0)
+    vals, meta = oracle.prune_compress(c.A, a_type)
+    alpha, beta = (1.0, 1.0) if a_type == wl.I8 else (0.75, -1.25)
+    check_gemm_full(pkg, vals, meta, a_type, c.B, b_type, c.C, alpha, beta, KBLOCK, KN)
+
+
 @pytest.mark.parametrize("N", [48, 320])
 def test_gemm_bias_f32_out(pkg, N):
     _say(f"gemm bias fp32 out N={N}")
