@@ -353,7 +353,7 @@ __device__ __forceinline__ void phase_end() {
 
 // MODE 0: streaming output stores (more tiles than compute units).  MODE 1
 // and 2 (every tile runs at once; K-blocked layout): ordinary output stores,
-// and in MODE 2 (beta != 0) also PF: during the last k-steps every wave also reads
+// and in MODE 2 (beta != 0) also PF: during the main loop every wave also reads
 // one 1 KiB piece of the tile's C per step (a tile row of a 32-bit C, two
 // rows of a 16-bit one) into a scratch kilobyte of LDS that nothing reads, so
 // that the epilogue finds C in the caches.  With every tile reaching its
@@ -422,8 +422,12 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
   // 16-bit one (lanes 0-31 the first, 32-63 the second).  The launcher uses
   // PF only when 256 rows of C span less than 2 GiB, so every offset fits in
   // 32 bits; rows past M fall outside the range, and a lane past N reads
-  // other bytes of C, which only warms the caches.  The window is the last
-  // 32 load steps (loads are issued up to step nsteps + 2).
+  // other bytes of C, which only warms the caches.  The window opens 48
+  // load steps before the last one (loads are issued up to step nsteps + 2,
+  // so at step 0 for K up to 45 k-steps) and runs until the tile's pieces
+  // are read: 32 steps for a 32-bit C, 16 for a 16-bit one.  Against the
+  // last 32 steps: fp16 4096^3, beta = 1, 90.0 -> 88.5 us with C not in the
+  // caches, 89.9 -> 89.8 us with C left there by the call before.
   uint32_t voC = 0, pf_lds = 0;
   if constexpr (PF) {
     const int csize = ep.out == OUT_32 ? 4 : 2, lpr = csize == 4 ? 64 : 32;
@@ -431,7 +435,7 @@ __global__ __launch_bounds__(kThreads8) void gemm_large8_kernel(const char* __re
                        (uint64_t)((int64_t)min(M - m0, kBM) * N - n0) * csize);
     ta.pf_row_bytes = (uint32_t)(64 / lpr) * (uint32_t)N * (uint32_t)csize;
     ta.pf_pieces = kBM / (64 / lpr);
-    ta.pf_j0 = max(0, nsteps + 3 - 32);
+    ta.pf_j0 = max(0, nsteps + 3 - 48);
     voC = (uint32_t)(l / lpr) * (uint32_t)N * (uint32_t)csize + 16u * (uint32_t)(l % lpr);
     pf_lds = lds_addr((SP24_LDS char*)lPF);
   }
@@ -1011,7 +1015,9 @@ static hipError_t launch_op(const void* A_vals, const uint32_t* meta, const void
   const int tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
   // C read ahead during the main loop only when every tile runs at once (at
   // most one per compute unit), so that all epilogues would otherwise read C
-  // from HBM in the same burst: fp16 4096^3 with beta = 1 93.0 -> 87.1 us.
+  // from HBM in the same burst: fp16 4096^3 with beta = 1, C not in the
+  // caches, 93.3 -> 88.5 us (a C that the call before left in the caches
+  // loses 1.6 us: 88.2 against 89.8 us).
   // With more tiles the epilogues are spread out and the C read of each is
   // hidden by reading ahead in the epilogue itself, while the extra loads and
   // the C lines in the caches cost the main loop (fp16 8192^3, beta = 1:

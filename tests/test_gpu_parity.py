@@ -428,15 +428,16 @@ def test_gemm_out16_bias(pkg, out, a_type, b_type, N, with_bias, b_layout):
 def test_gemm_one_wave_modes(pkg, a_type, b_type, out, b_layout, k_tail, beta_zero):
     """A grid of at most one tile per compute unit, where the product stores
     its output with ordinary stores and, with beta != 0, reads the tile's C
-    ahead during its last 32 load steps: 40 or 41 k-steps (the window starts
-    inside the loop; with k_tail the last step is partial), ragged M and N
+    ahead during 32 (32-bit C) or 16 (16-bit C) of its load steps, from 48
+    before the last: 56 or 57 k-steps (the window opens and closes inside
+    the loop; with k_tail the last step is partial), ragged M and N
     (rows of the last pieces past M, columns past N), 32-bit and 16-bit C
     (one or two tile rows per piece), beta != 0 and beta == 0; every output
     against the oracle."""
     if a_type == wl.I8 and out is not None:
         pytest.skip("int8 has a 32-bit output only")
     M, N = 701, 528  # N % 16 == 0: 8-bit B stored K x N above N = 64 needs it
-    K = 40 * (64 if wl.ESIZE[a_type] == 2 else 128) + k_tail
+    K = 56 * (64 if wl.ESIZE[a_type] == 2 else 128) + k_tail
     _say(f"gemm one-wave modes a={a_type} out={out} b_layout={b_layout} K={K} beta_zero={beta_zero}")
     c = wl.random_case(53, M, N, K, a_type, b_type, beta=1.0)
     vals, meta = oracle.prune_compress(c.A, a_type)
