@@ -668,7 +668,7 @@ def main():
     if not args.no_cpu:
         rows = args.cpu_rows
         if rows is None:
-            # the oracle does ~2e9 multiply-adds per second per core on the GPU machine's
+            # the oracle does ~2e9 multiply-adds per second per core on an MI355X
             # host (measured): ~4.8e11 of them is ~15 s on 16 cores (capped at all M rows)
             rows = max(1, min(w.M, int(4.8e11 / max(1, w.N * w.K // 2))))
         res["cpu_baseline"] = cpu_baseline(w, rows)
