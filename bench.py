@@ -49,6 +49,8 @@ def region_open(name, key):
 def region_close(name):
     r = REGIONS[name]
     r["end"] = CALLS[r["calls_of"]]
+
+
 # the headline metric (the default workload); other workloads name themselves
 METRIC = "dense-equiv TFLOP/s of 2:4 sparse GEMM (fp16, 8192^3) + % of smfmac peak"
 
